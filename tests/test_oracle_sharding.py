@@ -1,0 +1,238 @@
+"""Pins of the oracle's rank-level composition (oracle.step) against what the
+pages fix about sharding:
+  * page "04 · 分布式优化器", §2/§3: each rank updates only its range and the
+    ranks together cover the buffer, so the union of the D rank steps must
+    equal the unsharded step, bit for bit (the "simulate the shards on the
+    CPU in sequence and compare with the dense result" pattern of the page
+    "Megatron-LM 与 ZeRO", section "最小语义 reference");
+  * §5: force_all_reduce yields the full reduced buffer, whose restriction
+    to rank r's range is rank r's reduce-scatter;
+  * §4.3: the write-back touches the owned range only.
+"""
+
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.layout as L
+import oracle.numerics as N
+import oracle.step as S
+import workloads as W
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+
+
+def bf16(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+
+
+def make_inputs(lay, rng, sigma=1e-2, zero_padding=True):
+    Nn = lay.buffer_numel
+    D = lay.dp_size
+    grads = [bf16(rng.standard_normal(Nn) * sigma) for _ in range(D)]
+    if zero_padding:
+        owned = np.zeros(Nn, bool)
+        for r in lay.param_world:
+            owned[r.start:r.end] = True
+        for g in grads:
+            g[~owned] = 0
+    master = (rng.standard_normal(Nn) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(Nn) * 1e-3).astype(np.float32)
+    v = ((rng.standard_normal(Nn) * 1e-3) ** 2).astype(np.float32)
+    return grads, master, m, v
+
+
+def sharded_vs_unsharded(lay, grads, master, m, v, scale, t, grad_coords=S.WORLD, param_coords=S.WORLD):
+    hp = N.hp_array(HP, t)
+    Nn = lay.buffer_numel
+    # unsharded
+    mw, mm, vv = master.copy(), m.copy(), v.copy()
+    pw = np.full(Nn, 0x7FBF, np.uint16)
+    S.unsharded_step(lay, grads, scale, mw, mm, vv, hp, pw)
+    # sharded, rank by rank
+    ms, ms_m, ms_v = master.copy(), m.copy(), v.copy()
+    ps = np.full(Nn, 0x7FBF, np.uint16)
+    for r in range(lay.dp_size):
+        sm = S.gather_shard(lay, r, ms)
+        sm_m = S.gather_shard(lay, r, ms_m)
+        sm_v = S.gather_shard(lay, r, ms_v)
+        reps = grads if grad_coords == S.WORLD else [S.local_slices(lay, r, g) for g in grads]
+        if param_coords == S.WORLD:
+            S.rank_step(lay, r, reps, grad_coords, scale, sm, sm_m, sm_v, hp, ps, S.WORLD)
+        else:
+            pl = np.full(L.shard_numel(lay, r), 0x7FBF, np.uint16)
+            S.rank_step(lay, r, reps, grad_coords, scale, sm, sm_m, sm_v, hp, pl, S.LOCAL)
+            S.scatter_shard(lay, r, pl, ps)
+        S.scatter_shard(lay, r, sm, ms)
+        S.scatter_shard(lay, r, sm_m, ms_m)
+        S.scatter_shard(lay, r, sm_v, ms_v)
+    for a, b in ((mw, ms), (mm, ms_m), (vv, ms_v)):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.array_equal(pw, ps)
+    return ms, ms_m, ms_v, ps
+
+
+def test_tiny_ten_steps_union_equals_unsharded():
+    w = W.get("tiny")
+    lay = L.build_layout(w.param_numel, w.bucket_numel, w.dp_size)
+    rng = np.random.default_rng(1)
+    _, master, m, v = make_inputs(lay, rng)
+    m[:] = 0
+    v[:] = 0
+    for t in range(1, 11):
+        grads = [bf16(rng.standard_normal(1000) * w.grad_sigma) for _ in range(4)]
+        master, m, v, params = sharded_vs_unsharded(lay, grads, master, m, v, w.scale, t)
+    assert np.array_equal(params, bf16(master))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_layouts_union_equals_unsharded(seed):
+    rng = np.random.default_rng(seed)
+    pr = random.Random(seed)
+    sizes = [pr.randint(1, 300) for _ in range(pr.randint(1, 25))]
+    D = pr.choice([1, 2, 3, 4, 5, 8, 16])
+    lay = L.build_layout(sizes, pr.randint(1, 1500), D)
+    grads, master, m, v = make_inputs(lay, rng)
+    scale = pr.choice([1.0, 0.5, 1.0 / D, 1.0 / 3.0])
+    gc = pr.choice([S.WORLD, S.LOCAL])
+    pc = pr.choice([S.WORLD, S.LOCAL])
+    sharded_vs_unsharded(lay, grads, master, m, v, scale, pr.randint(1, 50), gc, pc)
+
+
+def test_split_parameter_is_updated_as_one():
+    # the Tiny workload's second parameter is cut 130 / 170 between ranks 0 and 1
+    w = W.get("tiny")
+    lay = L.build_layout(w.param_numel, w.bucket_numel, w.dp_size)
+    rng = np.random.default_rng(2)
+    grads, master, m, v = make_inputs(lay, rng)
+    ms, _, _, _ = sharded_vs_unsharded(lay, grads, master, m, v, 0.25, 1)
+    whole_m, whole_mm, whole_v = master[120:420].copy(), m[120:420].copy(), v[120:420].copy()
+    N.step([g[120:420] for g in grads], 0.25, whole_m, whole_mm, whole_v, N.hp_array(HP, 1))
+    assert np.array_equal(ms[120:420], whole_m)
+
+
+def test_all_reduce_restricted_is_reduce_scatter():
+    pr = random.Random(9)
+    rng = np.random.default_rng(9)
+    for _ in range(10):
+        sizes = [pr.randint(1, 200) for _ in range(pr.randint(1, 20))]
+        D = pr.choice([2, 3, 4, 7, 16])
+        lay = L.build_layout(sizes, pr.randint(1, 800), D)
+        grads = [bf16(rng.standard_normal(lay.buffer_numel)) for _ in range(D)]
+        full = S.all_reduce(grads, 0.5)
+        union = np.full(lay.buffer_numel, 0xFFFF, np.uint16)
+        for r in range(D):
+            out_w = np.full(lay.buffer_numel, 0xFFFF, np.uint16)
+            S.reduce_scatter(lay, r, grads, S.WORLD, 0.5, out_w, S.WORLD)
+            mine = np.zeros(lay.buffer_numel, bool)
+            for rg, _ in L.rank_ranges(lay, r):
+                mine[rg.start:rg.end] = True
+            assert np.array_equal(out_w[mine], full[mine])
+            assert (out_w[~mine] == 0xFFFF).all()
+            union[mine] = out_w[mine]
+            # LOCAL coordinates hold the same values at the shard positions
+            out_l = np.full(L.shard_numel(lay, r), 0xFFFF, np.uint16)
+            S.reduce_scatter(lay, r, grads, S.WORLD, 0.5, out_l, S.LOCAL)
+            assert np.array_equal(out_l, S.local_slices(lay, r, out_w, fill=0xFFFF))
+        assert np.array_equal(union, full)
+
+
+def test_fused_equals_reduce_then_prereduced_step():
+    # reduce-scatter first, then the step with the one pre-reduced contribution and scale 1
+    w = W.get("tiny")
+    lay = L.build_layout([7, 33, 64, 5, 91], 100, 4)
+    rng = np.random.default_rng(4)
+    grads, master, m, v = make_inputs(lay, rng)
+    hp = N.hp_array(HP, 3)
+    for r in range(4):
+        a = [S.gather_shard(lay, r, x) for x in (master, m, v)]
+        b = [x.copy() for x in a]
+        pa = np.zeros(lay.buffer_numel, np.uint16)
+        pb = np.zeros(lay.buffer_numel, np.uint16)
+        S.rank_step(lay, r, grads, S.WORLD, 0.25, *a, hp, pa, S.WORLD)
+        red = np.zeros(lay.buffer_numel, np.uint16)
+        S.reduce_scatter(lay, r, grads, S.WORLD, 0.25, red, S.WORLD)
+        S.rank_step(lay, r, [red], S.WORLD, 1.0, *b, hp, pb, S.WORLD)
+        for x, y in zip(a, b):
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+        assert np.array_equal(pa, pb)
+    del w
+
+
+def test_writeback_touches_owned_range_only():
+    lay = L.build_layout([13, 300, 2, 77], 150, 4)    # two buckets, padding in each
+    rng = np.random.default_rng(5)
+    grads, master, m, v = make_inputs(lay, rng)
+    hp = N.hp_array(HP, 1)
+    owned_any = np.zeros(lay.buffer_numel, bool)
+    for r in range(4):
+        p = np.full(lay.buffer_numel, 0x7FBF, np.uint16)
+        sm = [S.gather_shard(lay, r, x) for x in (master, m, v)]
+        S.rank_step(lay, r, grads, S.WORLD, 0.25, *sm, hp, p, S.WORLD)
+        mine = np.zeros(lay.buffer_numel, bool)
+        for pc in L.rank_pieces(lay, r):
+            mine[pc.gbuf_world.start:pc.gbuf_world.end] = True
+        assert (p[~mine] == 0x7FBF).all()
+        assert (p[mine] != 0x7FBF).all()
+        owned_any |= mine
+        # writeback of the updated master gives the same bytes
+        q = np.full(lay.buffer_numel, 0x7FBF, np.uint16)
+        S.writeback(lay, r, sm[0], q, S.WORLD)
+        assert np.array_equal(p, q)
+    # every parameter element is owned by someone; padding by no one
+    params = np.zeros(lay.buffer_numel, bool)
+    for rg in lay.param_world:
+        params[rg.start:rg.end] = True
+    assert np.array_equal(owned_any, params)
+
+
+def test_resume_is_bit_exact():
+    w = W.get("tiny")
+    lay = L.build_layout(w.param_numel, w.bucket_numel, w.dp_size)
+    rng = np.random.default_rng(6)
+    steps = [[bf16(rng.standard_normal(1000) * 1e-2) for _ in range(4)] for _ in range(10)]
+    master0 = (rng.standard_normal(1000) * 0.02).astype(np.float32)
+    for r in range(4):
+        st = [S.gather_shard(lay, r, master0), np.zeros(252, np.float32), np.zeros(252, np.float32)]
+        st = [np.resize(x, L.shard_numel(lay, r)) for x in st]
+        a = [x.copy() for x in st]
+        for t in range(1, 11):
+            S.rank_step(lay, r, steps[t - 1], S.WORLD, 0.25, *a, N.hp_array(HP, t))
+        b = [x.copy() for x in st]
+        for t in range(1, 6):
+            S.rank_step(lay, r, steps[t - 1], S.WORLD, 0.25, *b, N.hp_array(HP, t))
+        saved = [x.tobytes() for x in b]
+        b = [np.frombuffer(s, np.float32).copy() for s in saved]
+        for t in range(6, 11):
+            S.rank_step(lay, r, steps[t - 1], S.WORLD, 0.25, *b, N.hp_array(HP, t))
+        for x, y in zip(a, b):
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+def test_segmentation_invariance():
+    # per-piece calls and one call per contiguous owned run give the same bytes
+    lay = L.build_layout([5, 17, 1, 1, 40, 3, 260, 9], 64, 4)
+    rng = np.random.default_rng(8)
+    grads, master, m, v = make_inputs(lay, rng)
+    hp = N.hp_array(HP, 2)
+    for r in range(4):
+        a = [S.gather_shard(lay, r, x) for x in (master, m, v)]
+        b = [x.copy() for x in a]
+        pa = np.zeros(lay.buffer_numel, np.uint16)
+        pb = np.zeros(lay.buffer_numel, np.uint16)
+        S.rank_step(lay, r, grads, S.WORLD, 0.25, *a, hp, pa, S.WORLD)
+        runs = []
+        for pc in L.rank_pieces(lay, r):
+            if runs and runs[-1][1] == pc.gbuf_world.start:
+                runs[-1][1] = pc.gbuf_world.end
+            else:
+                runs.append([pc.gbuf_world.start, pc.gbuf_world.end, pc.shard_offset])
+        for ws, we, k0 in runs:
+            k1 = k0 + we - ws
+            N.step([g[ws:we] for g in grads], 0.25, b[0][k0:k1], b[1][k0:k1], b[2][k0:k1], hp, pb[ws:we])
+        for x, y in zip(a, b):
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+        assert np.array_equal(pa, pb)

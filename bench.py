@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Throughput of one DP rank's sharded Adam step on one MI355X.
+
+A step is one sharded_adam_step call on the rank's shard: reduce the D
+replica contributions (scaled, fixed rank order), Adam on the fp32
+master/m/v shard, bf16 write-back into the owned range; one fused kernel.
+Default workload: GPT-2-small-shaped parameter list (124,439,808 elements,
+buckets of 40,000,000, D = 8), rank 1's shard (15,554,976 elements), 8 full
+bf16 replica buffers in HBM.
+
+Prints one JSON line: elements/s of the step (wall clock over the timed
+steps), the HBM roofline of the step kernel (algorithmic bytes (2D+26) per
+owned element over its average duration, from HIP events on the launch
+stream), and the CPU oracle timed on a bounded sample beside it.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--rank R]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sharded Adam step: elements/s and HBM GB/s (% of peak) at 1 MI355X"
+PEAK_HBM_GBPS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "zero_distributed_optimizer_amd", "csrc", "kernels.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str) -> float | None:
+    """HBM bytes per launch of the step kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or
+    None if there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"sharded_adam_step_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not src or not val or src.group(1) != kernel_source_hash():
+        return None
+    return float(val.group(1))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gpt2_small")
+    ap.add_argument("--rank", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only: the D ranks' contributions are D "
+                          "replica buffers in one GPU's HBM; run with --gpus 1"}), flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    import zero_distributed_optimizer_amd as zdo
+
+    zdo.require_library()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    w = W.get(args.workload)
+    rank = w.time_ranks[0] if args.rank is None else args.rank
+    D = w.dp_size
+    plan = zdo.build_range_map(w.param_numel, w.bucket_numel, D, rank)
+    N, Ln, E = plan.buffer_numel, plan.shard_numel, plan.owned_numel
+    coords = zdo.WORLD if w.grad_mode == "world" else zdo.LOCAL
+    n_rep = N if coords == zdo.WORLD else Ln
+    stride = (n_rep + 7) // 8 * 8
+    log(f"workload {w.name}: N={N} D={D} rank={rank} E={E} L={Ln} grads={w.grad_mode}")
+
+    # inputs, resident in HBM before the timed region
+    t0 = time.perf_counter()
+    rep_buf = torch.empty(D * stride, dtype=torch.bfloat16, device=dev)
+    reps = []
+    for j in range(D):
+        s = rep_buf[j * stride: j * stride + n_rep]
+        W.normal_bf16(n_rep, w.grad_sigma, W.seed(w.cfg, 0, "grad", j), out=s,
+                      probe_fraction=w.probe_fraction, probe_seed=W.seed(w.cfg, 0, "probe", j))
+        reps.append(s.view(torch.int16))
+    master = W.normal_f32(Ln, w.master_sigma, W.seed(w.cfg, 0, "master"), dev)
+    exp_avg = W.normal_f32(Ln, w.m_sigma, W.seed(w.cfg, 0, "m"), dev)
+    exp_avg_sq = W.square_normal_f32(Ln, w.v_sigma, W.seed(w.cfg, 0, "v"), dev)
+    params = torch.zeros(n_rep, dtype=torch.int16, device=dev)
+    torch.cuda.synchronize(dev)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f}s")
+
+    stream = torch.cuda.current_stream(dev)
+    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
+
+    def step(t: int) -> None:
+        zdo.sharded_adam_step(plan, reps, coords, w.scale, master, exp_avg, exp_avg_sq, params, coords,
+                              step=t, stream=stream, **hp)
+
+    t = 0
+    for _ in range(args.warmup):
+        t += 1
+        step(t)
+    torch.cuda.synchronize(dev)
+
+    # timed region: K back-to-back steps, a HIP event pair around every launch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        t += 1
+        ev[i][0].record(stream)
+        step(t)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - w0
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    kern_avg_s = float(np.mean(kern_ms)) / 1e3
+    bytes_per_elem = 2 * D + 26
+    alg_bytes = E * bytes_per_elem
+    achieved = alg_bytes / kern_avg_s / 1e9
+    log(f"step: wall {ms_per_step * 1e3:.1f} us/step, kernel avg {kern_avg_s * 1e6:.1f} us "
+        f"(p10 {np.percentile(kern_ms, 10) * 1e3:.1f}, p90 {np.percentile(kern_ms, 90) * 1e3:.1f}), "
+        f"{achieved:.0f} GB/s algorithmic")
+
+    # plain-copy reference on the same stream (1 GiB read + 1 GiB write)
+    nb = 1 << 30
+    src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        zdo.device_copy(dst, src, stream)
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for a, b in cev:
+        a.record(stream)
+        zdo.device_copy(dst, src, stream)
+        b.record(stream)
+    torch.cuda.synchronize(dev)
+    copy_gbps = 2 * nb / (float(np.mean([a.elapsed_time(b) for a, b in cev])) / 1e3) / 1e9
+    del src, dst
+    log(f"copy reference: {copy_gbps:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(plan, w, reps, coords, master, exp_avg, exp_avg_sq, args.cpu_seconds)
+
+    traffic = traffic_from_profiles(w.name)
+    out = {
+        "metric": METRIC,
+        "value": E / (ms_per_step / 1e3),
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "params": len(w.param_numel),
+            "buffer_elements": N,
+            "bucket_elements": w.bucket_numel,
+            "buckets": int(plan.buckets().size),
+            "dp_size": D,
+            "rank": rank,
+            "owned_elements": E,
+            "grad_replicas": f"{D} x bf16 {'whole buffers' if coords == zdo.WORLD else 'shard slices'}",
+            "state": "fp32 master/exp_avg/exp_avg_sq shard",
+            "bytes_per_element": bytes_per_elem,
+        },
+        "hbm_gbps": alg_bytes / (ms_per_step / 1e3) / 1e9,
+        "hbm_frac_of_peak": alg_bytes / (ms_per_step / 1e3) / 1e9 / PEAK_HBM_GBPS,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS,
+            "traffic": traffic,
+        },
+        "kernel": {"name": "step_kernel", "avg_us": kern_avg_s * 1e6,
+                   "p10_us": float(np.percentile(kern_ms, 10)) * 1e3,
+                   "p90_us": float(np.percentile(kern_ms, 90)) * 1e3,
+                   "source_sha256_16": kernel_source_hash()},
+        "copy_reference_gbps": copy_gbps,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(plan, w, reps, coords, master, exp_avg, exp_avg_sq, seconds: float) -> dict:
+    """The oracle (oracle/step.c through oracle.step.rank_step) on the host
+    cores, over the same rank's whole shard, repeated for about `seconds`;
+    only the step compute is timed."""
+    import numpy as np
+
+    import oracle.layout as OL
+    import oracle.numerics as ON
+    import oracle.step as OS
+
+    t0 = time.perf_counter()
+    lay = OL.build_layout(w.param_numel, w.bucket_numel, w.dp_size)
+    r = plan.rank
+    reps_h = [x.cpu().numpy().view(np.uint16) for x in reps]
+    st = [x.cpu().numpy().copy() for x in (master, exp_avg, exp_avg_sq)]
+    par = np.zeros(reps_h[0].size, np.uint16)
+    log(f"cpu baseline: host copies in {time.perf_counter() - t0:.1f}s, {ON.threads()} threads")
+    passes, spent, t = 0, 0.0, 0
+    while spent < seconds or passes < 1:
+        t += 1
+        hp = ON.hp_array(w.hp, t)
+        a = time.perf_counter()
+        OS.rank_step(lay, r, reps_h, coords, w.scale, *st, hp, par, coords)
+        spent += time.perf_counter() - a
+        passes += 1
+    E = plan.owned_numel
+    log(f"cpu baseline: {passes} passes in {spent:.1f}s")
+    return {"value": E * passes / spent, "unit": "elements/s", "cores": ON.threads(), "kind": "oracle",
+            "sample": f"rank {r}'s whole shard of {w.name} ({E} elements, D={w.dp_size}), {passes} passes, "
+                      f"{spent:.1f} s of step compute (host copies excluded)",
+            "gbps": E * (2 * w.dp_size + 26) * passes / spent / 1e9}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,196 @@
+/*
+ * zdo.h — one data-parallel rank's share of a distributed-optimizer step
+ * (ZeRO-1 style, as in Megatron-LM's DistributedOptimizer) on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method (page "04 · 分布式优化器", a Megatron-LM code-reading chapter):
+ * the grads of one dtype live in one flat 1-D buffer cut into buckets (§2);
+ * each bucket is padded to a multiple of the DP size D (§5) and split into D
+ * equal contiguous ranges, rank r owning range r whatever parameters it cuts
+ * (§2, §3); the grads are scaled (§5), reduce-scattered so each rank keeps
+ * the sum over its range (§4.2), copied into the rank's fp32 main-grad
+ * shard through the four-way range map (§4.1, §4.3), Adam runs on the fp32
+ * master/m/v shard only (§4.3), and the updated parameters are written back
+ * as bf16 into the owned range of the parameter buffer (§4.3).
+ * force_all_reduce produces the whole reduced buffer instead (§5).
+ *
+ * On one GPU, the D ranks' contributions are D replica buffers in this
+ * GPU's memory; the library sums them itself (no collective library).
+ *
+ * Conventions for every call:
+ *   - bf16 values are passed as uint16_t bit patterns.
+ *   - Device pointers are caller-owned, must be 16-byte aligned, and point
+ *     to memory of the device the plan was built on. Host arrays (the
+ *     replica pointer list, param_numel, hp) are read during the call only.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Calls that take
+ *     one only enqueue work on it and return; they never allocate device
+ *     memory and never synchronise the host.
+ *   - Coordinates of a buffer: ZDO_WORLD indexes the whole padded buffer
+ *     [0, N); ZDO_LOCAL indexes the rank's shard [0, L).
+ *   - Every call returns ZDO_OK (0) or a negative ZDO_E* code; the message of
+ *     the last failing call on this thread is zdo_last_error(). No call
+ *     aborts or throws. Faults inside a kernel surface when the caller
+ *     synchronises the stream.
+ *
+ * Arithmetic (fixed, so results are reproducible bit for bit):
+ *   per owned element w:  s_j = bf16(fp32(g_j[w]) * scale), j = 0..n-1
+ *                         acc = s_0 + s_1 + ... + s_{n-1}   (fp32, this order)
+ *                         g   = fp32(bf16(acc))
+ *   Adam (Kingma & Ba, Algorithm 1, with weight decay decoupled and scaled by
+ *   lr as in Loshchilov & Hutter), each step one fp32 IEEE operation, no FMA:
+ *     m' = b1*m + (1-b1)*g        v' = b2*v + (1-b2)*(g*g)
+ *     p' = p - lr*( (m'/bc1) / (sqrt(v'/bc2) + eps) + wd*p )
+ *   with 1-b1, 1-b2 in fp32 and bc_i = 1 - b_i^t computed in double by t
+ *   products and rounded once. bf16() is round-to-nearest-even, overflow to
+ *   Inf, subnormals kept, NaN stays NaN.
+ */
+#ifndef ZDO_H
+#define ZDO_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZDO_OK 0
+#define ZDO_EINVAL (-1)   /* bad argument (size, rank, coords, count, NULL) */
+#define ZDO_EALIGN (-2)   /* a device pointer is not 16-byte aligned */
+#define ZDO_EALIAS (-3)   /* outputs overlap each other or the inputs illegally */
+#define ZDO_EHIP (-4)     /* HIP runtime or launch failure; no device for the plan */
+#define ZDO_ENOMEM (-5)   /* host or device allocation failed */
+
+#define ZDO_WORLD 0
+#define ZDO_LOCAL 1
+
+#define ZDO_MAX_REPLICAS 64   /* largest D (and replica count) a launch accepts */
+
+typedef struct zdo_plan zdo_plan;
+
+/* Half-open [start, end) of element indices (page 1, §4.1 "Range"). */
+typedef struct {
+    int64_t start, end;
+} zdo_range;
+
+/* One parameter's piece inside the rank's range of one bucket (page 1,
+ * §4.1): the same elements described four ways, all translations of one
+ * another. shard_offset is where gbuf_world.start sits in the rank's fp32
+ * shard (master/m/v/main grad, LOCAL coordinates). 80 bytes, no padding. */
+typedef struct {
+    int32_t param_index, bucket_index;
+    zdo_range gbuf_world;            /* in the whole buffer */
+    zdo_range gbuf_world_in_bucket;  /* relative to the bucket start */
+    zdo_range gbuf_local;            /* relative to the rank's range start */
+    zdo_range param;                 /* inside the parameter itself */
+    int64_t shard_offset;
+} zdo_piece;
+
+/* One bucket. shard_numel = padded_numel / D; the rank's range of the bucket
+ * is [offset + rank*shard_numel, +shard_numel) in WORLD coordinates and
+ * [shard_base, shard_base + shard_numel) in LOCAL coordinates. */
+typedef struct {
+    int64_t offset, numel, padded_numel, shard_numel, shard_base;
+} zdo_bucket;
+
+/* Adam hyper-parameters for one step; step is t >= 1. */
+typedef struct {
+    float lr, beta1, beta2, eps, weight_decay;
+    int32_t reserved;   /* must be 0 */
+    int64_t step;
+} zdo_adam;
+
+/* ---- plan: layout and range map (host) ----------------------------------- */
+
+/* Lays out n_params parameters of the given element counts (each >= 1) in
+ * order in one flat buffer; cuts buckets greedily (a bucket closes right after
+ * the parameter that brings it to >= bucket_numel elements, or after the last
+ * parameter; a parameter never spans two buckets); pads each bucket at its
+ * tail to a multiple of dp_size; and builds rank `rank`'s range map (page 1,
+ * §2, §3, §4.1, §5). The rank's fp32 shard places each bucket's local view at
+ * the first slot >= the previous view's end that is congruent to the range's
+ * WORLD start modulo 8, so every LOCAL index is congruent to its WORLD index
+ * modulo 8 (gap slots, < 8 per bucket, and padding slots are never touched).
+ * If a HIP device is present, the plan's segment table is uploaded to the
+ * current device (the plan's device); otherwise the plan is host-only and
+ * the launch calls fail with ZDO_EHIP. *out receives the plan, owned by the
+ * caller until zdo_plan_destroy. Errors: ZDO_EINVAL (n_params < 1, a size
+ * < 1, bucket_numel < 1, dp_size < 1 or > ZDO_MAX_REPLICAS, rank outside
+ * [0, dp_size), NULL), ZDO_ENOMEM, ZDO_EHIP (upload failed). */
+int build_range_map(const int64_t *param_numel, int32_t n_params, int64_t bucket_numel,
+                    int32_t dp_size, int32_t rank, zdo_plan **out);
+
+void zdo_plan_destroy(zdo_plan *plan);
+
+int64_t zdo_plan_buffer_numel(const zdo_plan *plan);  /* N: padded buffer length */
+int64_t zdo_plan_shard_numel(const zdo_plan *plan);   /* L: shard length, gaps and padding included */
+int64_t zdo_plan_owned_numel(const zdo_plan *plan);   /* E: parameter elements the rank owns */
+int32_t zdo_plan_dp_size(const zdo_plan *plan);
+int32_t zdo_plan_rank(const zdo_plan *plan);
+
+/* Two-call queries: with out == NULL (or cap too small) only *n is set. */
+int zdo_plan_buckets(const zdo_plan *plan, zdo_bucket *out, int32_t cap, int32_t *n);
+int zdo_plan_pieces(const zdo_plan *plan, zdo_piece *out, int64_t cap, int64_t *n);
+
+/* ---- device work ---------------------------------------------------------- */
+
+/* Reduce-scatter of the D contributions over the rank's whole range of every
+ * bucket, padding included (page 1, §4.2, with the scaling of §5 first).
+ * replicas: host array of n_replicas (== D) device pointers, each a bf16
+ * buffer of N (replica_coords = ZDO_WORLD) or L (ZDO_LOCAL) elements.
+ * out: bf16, N elements (out_coords = ZDO_WORLD) or L (ZDO_LOCAL); only the
+ * rank's ranges are written. out may coincide exactly with one replica when
+ * both use the same coordinates (in place, like a reduce-scatter into the
+ * grad buffer's own local view); any other overlap is ZDO_EALIAS. */
+int reduce_scatter_local(const zdo_plan *plan, const uint16_t *const *replicas, int32_t n_replicas,
+                         int32_t replica_coords, float scale, uint16_t *out, int32_t out_coords,
+                         void *stream);
+
+/* All-reduce of the D contributions over the whole padded buffer (page 1, §5,
+ * force_all_reduce: the full reduced grads instead of the rank's share).
+ * Same arithmetic as reduce_scatter_local; independent of the rank.
+ * replicas: n_replicas (== D) device bf16 buffers of N elements. out_full:
+ * bf16, N elements; it may coincide exactly with one replica. */
+int force_all_reduce(const zdo_plan *plan, const uint16_t *const *replicas, int32_t n_replicas,
+                     float scale, uint16_t *out_full, void *stream);
+
+/* The rank's optimizer step, fused: reduce the n_grads contributions over
+ * every owned parameter element, copy into the fp32 main grad through the
+ * range map, Adam on master/exp_avg/exp_avg_sq, and write bf16(master') into
+ * param_out (page 1, §4.2, §4.3, §5). Padding and elements of other ranks
+ * are neither read from the state nor written anywhere.
+ * grads: host array of n_grads device pointers; n_grads == D (the replicas)
+ * or 1 (an already reduced buffer, e.g. the output of reduce_scatter_local
+ * or force_all_reduce, with scale 1 to leave it unchanged), bf16 of N
+ * (grad_coords ZDO_WORLD) or L (ZDO_LOCAL) elements.
+ * master, exp_avg, exp_avg_sq: fp32, L elements each (LOCAL), updated in
+ * place; pairwise disjoint. param_out: bf16, N (param_coords ZDO_WORLD) or L
+ * (ZDO_LOCAL) elements, or NULL to skip the write-back. main_grad_out: fp32,
+ * L elements, or NULL; receives the fp32 main grad (a debugging output).
+ * hp: host pointer; hp->step >= 1. Outputs must not overlap each other or
+ * the grads (ZDO_EALIAS). */
+int sharded_adam_step(const zdo_plan *plan, const uint16_t *const *grads, int32_t n_grads,
+                      int32_t grad_coords, float scale, float *master, float *exp_avg,
+                      float *exp_avg_sq, uint16_t *param_out, int32_t param_coords,
+                      const zdo_adam *hp, float *main_grad_out, void *stream);
+
+/* bf16(master) into the owned parameter elements of param_out (page 1, §4.3:
+ * the updated master shard copied back into the buffer's owned range).
+ * master: fp32, L elements; param_out: bf16, N (ZDO_WORLD) or L (ZDO_LOCAL)
+ * elements; must not overlap. */
+int writeback_params(const zdo_plan *plan, const float *master, uint16_t *param_out,
+                     int32_t param_coords, void *stream);
+
+/* ---- measurement helper (not part of the method) -------------------------- */
+
+/* Plain device copy of `bytes` bytes (a multiple of 16) from src to dst,
+ * non-overlapping, both 16-byte aligned: the streaming-bandwidth and
+ * counter-calibration reference for the kernels above. */
+int zdo_device_copy(void *dst, const void *src, int64_t bytes, void *stream);
+
+const char *zdo_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZDO_H */

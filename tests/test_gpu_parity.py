@@ -1,0 +1,486 @@
+"""Parity of the HIP path (through the C-ABI) with the CPU oracle.
+
+Bar: range maps and every bf16 output bit-exact; fp32 master / exp_avg /
+exp_avg_sq within a relative 1e-6 (absolute 1e-9 near zero) and, by design,
+bit-exact too; NaN compared by NaN-ness only. Every input is seeded
+(workloads.py); the oracle always runs on the bytes the device received.
+"""
+
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.layout as OL
+import oracle.numerics as ON
+import oracle.step as OS
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0x7FBF
+DEV = "cuda"
+
+
+# ---- helpers ----------------------------------------------------------------------------
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16).copy()).to(DEV)
+    return torch.from_numpy(a.copy()).to(DEV)
+
+
+def host_u16(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def host_f32(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy()
+
+
+def assert_bf16(got: np.ndarray, want: np.ndarray, what: str):
+    gn = ((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)
+    wn = ((want & 0x7F80) == 0x7F80) & ((want & 0x7F) != 0)
+    assert np.array_equal(gn, wn), f"{what}: NaN positions differ"
+    bad = np.flatnonzero(got[~gn] != want[~gn])
+    assert bad.size == 0, f"{what}: {bad.size} bf16 mismatches, first at {bad[:5]}"
+
+
+def assert_f32(got: np.ndarray, want: np.ndarray, what: str):
+    gn, wn = np.isnan(got), np.isnan(want)
+    assert np.array_equal(gn, wn), f"{what}: NaN positions differ"
+    g, w = got[~gn], want[~gn]
+    with np.errstate(invalid="ignore"):
+        close = (g == w) | (np.abs(g.astype(np.float64) - w) <= np.maximum(1e-6 * np.abs(w.astype(np.float64)), 1e-9))
+    assert close.all(), f"{what}: {np.count_nonzero(~close)} outside rel 1e-6 / abs 1e-9"
+    bad = np.flatnonzero(g.view(np.uint32) != w.view(np.uint32))
+    assert bad.size == 0, f"{what}: {bad.size} fp32 values not bit-identical (within tolerance)"
+
+
+def hp_kwargs(hp: dict, t: int) -> dict:
+    return dict(lr=hp["lr"], beta1=hp["beta1"], beta2=hp["beta2"], eps=hp["eps"],
+                weight_decay=hp["weight_decay"], step=t)
+
+
+def bf16_host(rng, n, sigma=1e-2):
+    x = (rng.standard_normal(n) * sigma).astype(np.float32)
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def local_stride(L: int) -> int:
+    return max(8, (L + 7) // 8 * 8)
+
+
+def free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+# ---- rounding and reduction -----------------------------------------------------------------
+
+def test_bf16_rounding_through_reduce(gpu):
+    """D = 1: out = bf16(bf16(x) * scale); scales that produce ties, subnormals,
+    overflow to Inf, signed zeros and NaN, compared with the oracle."""
+    rng = np.random.default_rng(1)
+    n = 1 << 16
+    h = np.arange(n, dtype=np.uint32).astype(np.uint16)     # every bf16 pattern
+    plan = gpu.build_range_map([n], n, 1, 0)
+    rep = to_dev(h)
+    out = torch.empty(n, dtype=torch.int16, device=DEV)
+    scales = [1.0, 0.5, 2.0 ** -20, 2.0 ** -126, 3.0, 1.0 + 2.0 ** -8, 1.0 + 2.0 ** -23, 1.0 / 3.0,
+              2.0 ** 100, -1.0, 0.0, float(np.float32(rng.random())), 1e-38, 2.0 ** 127]
+    for s in scales:
+        s = float(np.float32(s))
+        gpu.reduce_scatter_local(plan, [rep], gpu.WORLD, s, out, gpu.WORLD)
+        want = ON.reduce([h], s)
+        assert_bf16(host_u16(out), want, f"scale {s!r}")
+    free()
+
+
+def test_allreduce_worked_example(gpu):
+    # distributed-training notes, section "AllReduce": [1,2],[2,3],[3,3] -> [6,8]
+    plan = gpu.build_range_map([2], 10, 3, 0)
+    assert plan.buffer_numel == 3
+    vals = [[1.0, 2.0, 0.0], [2.0, 3.0, 0.0], [3.0, 3.0, 0.0]]
+    reps = [torch.tensor(v, dtype=torch.bfloat16, device=DEV).view(torch.int16) for v in vals]
+    out = torch.full((8,), SENTINEL, dtype=torch.int16, device=DEV)
+    gpu.force_all_reduce(plan, reps, 1.0, out)
+    assert out.view(torch.bfloat16)[:3].float().tolist() == [6.0, 8.0, 0.0]
+    assert (host_u16(out)[3:] == SENTINEL).all()
+    free()
+
+
+def _random_layout(pr):
+    kind = pr.random()
+    if kind < 0.3:
+        sizes = [pr.randint(1, 20) for _ in range(pr.randint(1, 40))]
+    elif kind < 0.7:
+        sizes = [pr.randint(1, 9000) for _ in range(pr.randint(1, 30))]
+    else:
+        sizes = [pr.choice([1, 7, 8, 9, 2047, 2048, 2049, 60000]) for _ in range(pr.randint(1, 12))]
+    D = pr.choice([1, 2, 3, 4, 5, 7, 8, 16, 32, 33])
+    bucket = pr.randint(1, max(2, sum(sizes) // pr.choice([1, 2, 5])))
+    return sizes, bucket, D
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_reduce_scatter_random_layouts(gpu, seed):
+    pr = random.Random(seed)
+    rng = np.random.default_rng(seed)
+    sizes, bucket, D = _random_layout(pr)
+    lay = OL.build_layout(sizes, bucket, D)
+    N = lay.buffer_numel
+    reps_h = [bf16_host(rng, N) for _ in range(D)]
+    reps_d = [to_dev(r) for r in reps_h]
+    scale = pr.choice([1.0, 1.0 / D, 0.3, 2.0])
+    full = OS.all_reduce(reps_h, scale)
+    for r in sorted({0, D - 1, pr.randrange(D)}):
+        plan = gpu.build_range_map(sizes, bucket, D, r)
+        Ln = plan.shard_numel
+        for in_c in (gpu.WORLD, gpu.LOCAL):
+            src_h = reps_h if in_c == gpu.WORLD else [OS.local_slices(lay, r, x) for x in reps_h]
+            src_d = reps_d if in_c == gpu.WORLD else [to_dev(x) for x in src_h]
+            for out_c in (gpu.WORLD, gpu.LOCAL):
+                n_out = N if out_c == gpu.WORLD else Ln
+                out = torch.full((max(n_out, 8),), SENTINEL, dtype=torch.int16, device=DEV)
+                gpu.reduce_scatter_local(plan, src_d, in_c, scale, out, out_c)
+                want = np.full(max(n_out, 8), SENTINEL, np.uint16)
+                OS.reduce_scatter(lay, r, src_h, in_c, scale, want, out_c)
+                assert_bf16(host_u16(out), want, f"rs r={r} in={in_c} out={out_c}")
+        # restricted all-reduce == reduce-scatter
+        out = torch.empty(max(N, 8), dtype=torch.int16, device=DEV)
+        gpu.force_all_reduce(plan, reps_d, scale, out)
+        assert_bf16(host_u16(out)[:N], full, "force_all_reduce")
+    free()
+
+
+def test_reduce_scatter_in_place(gpu):
+    rng = np.random.default_rng(5)
+    sizes, bucket, D = [1000, 3, 4097, 20000, 5], 9000, 4
+    lay = OL.build_layout(sizes, bucket, D)
+    N = lay.buffer_numel
+    reps_h = [bf16_host(rng, N) for _ in range(D)]
+    for r in range(D):
+        plan = gpu.build_range_map(sizes, bucket, D, r)
+        reps_d = [to_dev(x) for x in reps_h]
+        gpu.reduce_scatter_local(plan, reps_d, gpu.WORLD, 0.25, reps_d[r], gpu.WORLD)
+        want = reps_h[r].copy()
+        OS.reduce_scatter(lay, r, reps_h, gpu.WORLD, 0.25, want, gpu.WORLD)
+        assert_bf16(host_u16(reps_d[r]), want, f"in-place r={r}")
+    # force_all_reduce in place into replica 0
+    plan = gpu.build_range_map(sizes, bucket, D, 0)
+    reps_d = [to_dev(x) for x in reps_h]
+    gpu.force_all_reduce(plan, reps_d, 0.25, reps_d[0])
+    assert_bf16(host_u16(reps_d[0]), OS.all_reduce(reps_h, 0.25), "far in place")
+    free()
+
+
+# ---- the fused step ----------------------------------------------------------------------------
+
+def run_rank_step(gpu, sizes, bucket, D, r, reps_h, state_h, scale, hp, t, grad_c, param_c, reps_d=None,
+                  with_main_grad=True):
+    """One step on the GPU and in the oracle; compare everything."""
+    lay = OL.build_layout(sizes, bucket, D)
+    plan = gpu.build_range_map(sizes, bucket, D, r)
+    N, Ln = plan.buffer_numel, plan.shard_numel
+    if grad_c == gpu.WORLD:
+        src_h = reps_h
+    else:
+        src_h = [OS.local_slices(lay, r, x) for x in reps_h]
+    if reps_d is None or grad_c == gpu.LOCAL:
+        reps_d = [to_dev(x) for x in src_h]
+    master, m, v = (to_dev(x) for x in state_h)
+    n_par = N if param_c == gpu.WORLD else Ln
+    par = torch.full((max(n_par, 8),), SENTINEL, dtype=torch.int16, device=DEV)
+    mg = torch.full((max(Ln, 8),), -7.0, dtype=torch.float32, device=DEV) if with_main_grad else None
+    gpu.sharded_adam_step(plan, reps_d, grad_c, scale, master, m, v, par, param_c, main_grad_out=mg,
+                          **hp_kwargs(hp, t))
+    want = [x.copy() for x in state_h]
+    want_par = np.full(max(n_par, 8), SENTINEL, np.uint16)
+    want_mg = np.full(max(Ln, 8), -7.0, np.float32) if with_main_grad else None
+    OS.rank_step(lay, r, src_h, grad_c, scale, *want, ON.hp_array(hp, t), want_par, param_c,
+                 None if want_mg is None else want_mg[:Ln])
+    for got, w, name in zip((master, m, v), want, ("master", "exp_avg", "exp_avg_sq")):
+        assert_f32(host_f32(got), w, f"{name} r={r}")
+    assert_bf16(host_u16(par), want_par, f"params r={r}")
+    if with_main_grad:
+        assert_f32(host_f32(mg), want_mg, f"main grad r={r}")
+    return [host_f32(x) for x in (master, m, v)], host_u16(par)
+
+
+def test_tiny_all_ranks_ten_steps(gpu):
+    """The Tiny workload: 1000 elements, D = 4, every rank, ten steps with
+    fresh grads each step; the one parameter the rank edge cuts (120 / 300)
+    and ranks whose shard starts off the 8-element phase."""
+    w = W.get("tiny")
+    lay = OL.build_layout(w.param_numel, w.bucket_numel, w.dp_size)
+    master0 = W.normal_f32(lay.buffer_numel, w.master_sigma, W.seed(1, 0, "master")).numpy()
+    for r in w.verify_ranks:
+        Ln = OL.shard_numel(lay, r)
+        state = [OS.gather_shard(lay, r, master0), np.zeros(Ln, np.float32), np.zeros(Ln, np.float32)]
+        for t in range(1, w.steps + 1):
+            reps = [W.bf16_bits(W.normal_bf16(1000, w.grad_sigma, W.seed(1, t, "grad", j)))
+                    for j in range(w.dp_size)]
+            state, par = run_rank_step(gpu, w.param_numel, w.bucket_numel, w.dp_size, r, reps, state, w.scale,
+                                       w.hp, t, gpu.WORLD, gpu.WORLD)
+    free()
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_fused_step_random_layouts(gpu, seed):
+    pr = random.Random(1000 + seed)
+    rng = np.random.default_rng(1000 + seed)
+    sizes, bucket, D = _random_layout(pr)
+    lay = OL.build_layout(sizes, bucket, D)
+    N = lay.buffer_numel
+    reps_h = [bf16_host(rng, N, pr.choice([1e-3, 1e-2, 1.0])) for _ in range(D)]
+    scale = pr.choice([1.0, 1.0 / D, 1.0 / 3.0, 0.5])
+    hp = dict(lr=pr.choice([1e-3, 3e-4]), beta1=0.9, beta2=pr.choice([0.999, 0.95]), eps=1e-8,
+              weight_decay=pr.choice([0.0, 0.01, 0.1]))
+    t = pr.choice([1, 2, 10, 1000])
+    for r in sorted({0, D - 1, pr.randrange(D)}):
+        Ln = OL.shard_numel(lay, r)
+        state = [(rng.standard_normal(Ln) * 0.02).astype(np.float32),
+                 (rng.standard_normal(Ln) * 1e-3).astype(np.float32),
+                 ((rng.standard_normal(Ln) * 1e-3) ** 2).astype(np.float32)]
+        run_rank_step(gpu, sizes, bucket, D, r, reps_h, state, scale, hp, t,
+                      pr.choice([gpu.WORLD, gpu.LOCAL]), pr.choice([gpu.WORLD, gpu.LOCAL]))
+    free()
+
+
+def test_rank_with_only_padding(gpu):
+    # 5 elements at D = 4: padded to 8, rank 3's range is all padding
+    rng = np.random.default_rng(3)
+    sizes, bucket, D = [3, 2], 100, 4
+    plan = gpu.build_range_map(sizes, bucket, D, 3)
+    assert plan.owned_numel == 0
+    reps = [to_dev(bf16_host(rng, 8)) for _ in range(D)]
+    st = [torch.full((8,), 1.5, dtype=torch.float32, device=DEV) for _ in range(3)]
+    par = torch.full((8,), SENTINEL, dtype=torch.int16, device=DEV)
+    gpu.sharded_adam_step(plan, reps, gpu.WORLD, 0.25, *st, par, gpu.WORLD, **hp_kwargs(W.get("tiny").hp, 1))
+    gpu.writeback_params(plan, st[0], par, gpu.WORLD)
+    torch.cuda.synchronize()
+    assert (host_u16(par) == SENTINEL).all()
+    assert all((host_f32(x) == 1.5).all() for x in st)
+    # its reduce-scatter still covers the padding of its range
+    out = torch.full((8,), SENTINEL, dtype=torch.int16, device=DEV)
+    gpu.reduce_scatter_local(plan, reps, gpu.WORLD, 1.0, out, gpu.WORLD)
+    want = np.full(8, SENTINEL, np.uint16)
+    OS.reduce_scatter(OL.build_layout(sizes, bucket, D), 3, [host_u16(x) for x in reps], 0, 1.0, want, 0)
+    assert_bf16(host_u16(out), want, "padding-only rs")
+    free()
+
+
+def test_prereduced_and_writeback_equal_fused(gpu):
+    """reduce_scatter_local (or force_all_reduce) then the step with the one
+    reduced buffer and scale 1, and the step without write-back followed by
+    writeback_params, give the fused step's bytes."""
+    rng = np.random.default_rng(9)
+    sizes, bucket, D = [5000, 17, 1, 30000, 2049, 999], 12000, 8
+    lay = OL.build_layout(sizes, bucket, D)
+    N = lay.buffer_numel
+    reps_h = [bf16_host(rng, N) for _ in range(D)]
+    reps_d = [to_dev(x) for x in reps_h]
+    hp = W.get("tiny").hp
+    for r in range(D):
+        plan = gpu.build_range_map(sizes, bucket, D, r)
+        Ln = plan.shard_numel
+        st0 = [(rng.standard_normal(Ln) * 0.02).astype(np.float32), np.zeros(Ln, np.float32),
+               np.zeros(Ln, np.float32)]
+        outs = []
+        for variant in ("fused", "rs", "far", "split"):
+            st = [to_dev(x) for x in st0]
+            par = torch.full((N,), SENTINEL, dtype=torch.int16, device=DEV)
+            if variant == "fused":
+                gpu.sharded_adam_step(plan, reps_d, gpu.WORLD, 0.125, *st, par, gpu.WORLD, **hp_kwargs(hp, 1))
+            elif variant == "rs":
+                red = torch.empty(Ln, dtype=torch.int16, device=DEV)
+                gpu.reduce_scatter_local(plan, reps_d, gpu.WORLD, 0.125, red, gpu.LOCAL)
+                gpu.sharded_adam_step(plan, [red], gpu.LOCAL, 1.0, *st, par, gpu.WORLD, **hp_kwargs(hp, 1))
+            elif variant == "far":
+                red = torch.empty(N, dtype=torch.int16, device=DEV)
+                gpu.force_all_reduce(plan, reps_d, 0.125, red)
+                gpu.sharded_adam_step(plan, [red], gpu.WORLD, 1.0, *st, par, gpu.WORLD, **hp_kwargs(hp, 1))
+            else:
+                gpu.sharded_adam_step(plan, reps_d, gpu.WORLD, 0.125, *st, None, gpu.WORLD, **hp_kwargs(hp, 1))
+                gpu.writeback_params(plan, st[0], par, gpu.WORLD)
+            outs.append(([host_f32(x) for x in st], host_u16(par)))
+        for (st, par), name in zip(outs[1:], ("rs", "far", "split")):
+            for a, b in zip(st, outs[0][0]):
+                assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), name
+            assert np.array_equal(par, outs[0][1]), name
+    free()
+
+
+def test_nan_inf_propagate(gpu):
+    rng = np.random.default_rng(10)
+    sizes, bucket, D = [300, 4000], 5000, 4
+    lay = OL.build_layout(sizes, bucket, D)
+    N = lay.buffer_numel
+    reps_h = [bf16_host(rng, N) for _ in range(D)]
+    nan, inf, ninf = 0x7FC1, 0x7F80, 0xFF80
+    for k, pos in enumerate(rng.choice(N, 60, replace=False)):
+        reps_h[k % D][pos] = (nan, inf, ninf)[k % 3]
+    for r in range(D):
+        Ln = OL.shard_numel(lay, r)
+        st = [(rng.standard_normal(Ln) * 0.02).astype(np.float32), np.zeros(Ln, np.float32),
+              np.zeros(Ln, np.float32)]
+        run_rank_step(gpu, sizes, bucket, D, r, reps_h, st, 0.25, W.get("tiny").hp, 1, gpu.WORLD, gpu.WORLD)
+    free()
+
+
+def test_error_paths(gpu):
+    Z = gpu
+    plan = Z.build_range_map([100, 28], 64, 2, 1)
+    x = torch.zeros(256, dtype=torch.int16, device=DEV)
+    f = torch.zeros(256, dtype=torch.float32, device=DEV)
+    g = torch.zeros(256, dtype=torch.float32, device=DEV)
+    h = torch.zeros(256, dtype=torch.float32, device=DEV)
+    hp = hp_kwargs(W.get("tiny").hp, 1)
+    with pytest.raises(Z.ZdoError) as e:
+        Z.reduce_scatter_local(plan, [x], Z.WORLD, 1.0, x, Z.WORLD)           # one replica, D = 2
+    assert e.value.code == Z.EINVAL
+    with pytest.raises(Z.ZdoError) as e:
+        Z.reduce_scatter_local(plan, [x, x], Z.WORLD, 1.0, x[8:], Z.WORLD)    # partial overlap
+    assert e.value.code == Z.EALIAS
+    with pytest.raises(Z.ZdoError) as e:
+        Z.reduce_scatter_local(plan, [x, x], 7, 1.0, x, Z.WORLD)
+    assert e.value.code == Z.EINVAL
+    with pytest.raises(Z.ZdoError) as e:
+        Z.sharded_adam_step(plan, [x, x], Z.WORLD, 1.0, f, f, h, None, **hp)   # master == exp_avg
+    assert e.value.code == Z.EALIAS
+    with pytest.raises(Z.ZdoError) as e:
+        Z.sharded_adam_step(plan, [x, x], Z.WORLD, 1.0, f[1:], g, h, None, **hp)   # misaligned
+    assert e.value.code == Z.EALIGN
+    with pytest.raises(Z.ZdoError) as e:
+        Z.sharded_adam_step(plan, [x, x, x], Z.WORLD, 1.0, f, g, h, None, **hp)    # 3 grads at D = 2
+    assert e.value.code == Z.EINVAL
+    with pytest.raises(Z.ZdoError) as e:
+        Z.sharded_adam_step(plan, [x, x], Z.WORLD, 1.0, f, g, h, x, Z.WORLD, **dict(hp, step=0))
+    assert e.value.code == Z.EINVAL
+    with pytest.raises(Z.ZdoError) as e:
+        Z.sharded_adam_step(plan, [x, x], Z.WORLD, 1.0, f, g, h, x, Z.WORLD, **dict(hp, beta2=1.0))
+    assert e.value.code == Z.EINVAL
+    with pytest.raises(Z.ZdoError) as e:
+        Z.writeback_params(plan, f, f.view(torch.int16)[:256], Z.WORLD)
+    assert e.value.code == Z.EALIAS
+    with pytest.raises(ValueError):
+        Z.sharded_adam_step(plan, [x, x], Z.WORLD, 1.0, f[:10], g, h, None, **hp)   # too small
+    torch.cuda.synchronize()
+    free()
+
+
+# ---- the five workloads at full size ---------------------------------------------------------
+
+def _gen_world(w, N, step=0):
+    reps = []
+    for j in range(w.dp_size):
+        t = torch.empty(N, dtype=torch.bfloat16, device=DEV)
+        W.normal_bf16(N, w.grad_sigma, W.seed(w.cfg, step, "grad", j), out=t,
+                      probe_fraction=w.probe_fraction, probe_seed=W.seed(w.cfg, step, "probe", j))
+        reps.append(t.view(torch.int16))
+    return reps
+
+
+def _gen_state(w, Ln):
+    master = W.normal_f32(Ln, w.master_sigma, W.seed(w.cfg, 0, "master"), DEV)
+    m = W.normal_f32(Ln, w.m_sigma, W.seed(w.cfg, 0, "m"), DEV)
+    v = W.square_normal_f32(Ln, w.v_sigma, W.seed(w.cfg, 0, "v"), DEV)
+    return master, m, v
+
+
+@pytest.mark.parametrize("name", ["gpt2_small", "frag"])
+def test_workload_every_rank_full_compare(gpu, name):
+    """GPT-2-small shape (D = 8) and the fragmentation stress (D = 16, +-65504
+    probes): every rank, every element compared; for the stress workload also
+    force_all_reduce over the whole buffer and the step on its output."""
+    w = W.get(name)
+    lay = OL.build_layout(w.param_numel, w.bucket_numel, w.dp_size)
+    N = lay.buffer_numel
+    reps_d = _gen_world(w, N)
+    reps_h = [host_u16(x) for x in reps_d]
+    hpk = hp_kwargs(w.hp, 1)
+    hpa = ON.hp_array(w.hp, 1)
+    far_h = far_d = None
+    if name == "frag":
+        plan0 = gpu.build_range_map(w.param_numel, w.bucket_numel, w.dp_size, 0)
+        far_d = torch.empty(N, dtype=torch.int16, device=DEV)
+        gpu.force_all_reduce(plan0, reps_d, w.scale, far_d)
+        far_h = host_u16(far_d)
+        assert_bf16(far_h, OS.all_reduce(reps_h, w.scale), "force_all_reduce (whole buffer)")
+    par = torch.full((N,), SENTINEL, dtype=torch.int16, device=DEV)
+    want_par = np.full(N, SENTINEL, np.uint16)
+    for r in w.verify_ranks:
+        plan = gpu.build_range_map(w.param_numel, w.bucket_numel, w.dp_size, r)
+        Ln = plan.shard_numel
+        st = _gen_state(w, Ln)
+        st_h = [host_f32(x) for x in st]
+        gpu.sharded_adam_step(plan, reps_d, gpu.WORLD, w.scale, *st, par, gpu.WORLD, **hpk)
+        OS.rank_step(lay, r, reps_h, OS.WORLD, w.scale, *st_h, hpa, want_par, OS.WORLD)
+        for got, want, nm in zip(st, st_h, ("master", "exp_avg", "exp_avg_sq")):
+            assert_f32(host_f32(got), want, f"{name} r={r} {nm}")
+        if far_d is not None:
+            st2 = _gen_state(w, Ln)
+            par2 = torch.full((N,), SENTINEL, dtype=torch.int16, device=DEV)
+            gpu.sharded_adam_step(plan, [far_d], gpu.WORLD, 1.0, *st2, par2, gpu.WORLD, **hpk)
+            for got, want, nm in zip(st2, st_h, ("master", "exp_avg", "exp_avg_sq")):
+                assert_f32(host_f32(got), want, f"{name} r={r} {nm} via force_all_reduce")
+            del st2, par2
+        del st
+    # all ranks wrote their owned ranges; padding keeps the sentinel
+    assert_bf16(host_u16(par), want_par, f"{name} params (all ranks)")
+    del reps_d, far_d, par
+    free()
+
+
+def _sample_slots(plan, rng, n):
+    """Owned LOCAL slots: random ones plus the first and last 16 of every piece."""
+    pcs = plan.pieces()
+    starts = pcs["shard_offset"].astype(np.int64)
+    lens = (pcs["gbuf_world"][:, 1] - pcs["gbuf_world"][:, 0]).astype(np.int64)
+    cum = np.concatenate([[0], np.cumsum(lens)])
+    pick = rng.integers(0, cum[-1], size=n)
+    pi = np.searchsorted(cum, pick, side="right") - 1
+    slots = starts[pi] + (pick - cum[pi])
+    edges = [np.arange(s, s + min(16, l)) for s, l in zip(starts, lens)] + \
+            [np.arange(s + max(0, l - 16), s + l) for s, l in zip(starts, lens)]
+    return np.unique(np.concatenate([slots] + edges))
+
+
+@pytest.mark.parametrize("name", ["llama3_8b", "llama3_70b"])
+def test_llama_shard_sampled(gpu, name):
+    """Llama-3-8B (D = 8) and Llama-3-70B (D = 32) shapes: one rank's shard
+    with its D replica slices in HBM (LOCAL coordinates), the full-size
+    launch; compared with the oracle on 2^20 sampled slots plus every piece's
+    first and last 16 elements."""
+    w = W.get(name)
+    r = w.verify_ranks[0]
+    plan = gpu.build_range_map(w.param_numel, w.bucket_numel, w.dp_size, r)
+    Ln = plan.shard_numel
+    stride = local_stride(Ln)
+    slices = torch.empty(w.dp_size * stride, dtype=torch.bfloat16, device=DEV)
+    reps = []
+    for j in range(w.dp_size):
+        s = slices[j * stride: j * stride + Ln]
+        W.normal_bf16(Ln, w.grad_sigma, W.seed(w.cfg, 0, "grad", j), out=s)
+        reps.append(s.view(torch.int16))
+    st = _gen_state(w, Ln)
+    par = torch.full((Ln,), SENTINEL, dtype=torch.int16, device=DEV)
+    rng = np.random.default_rng(w.cfg)
+    k = torch.from_numpy(_sample_slots(plan, rng, 1 << 20)).to(DEV)
+    before = [host_f32(x[k]) for x in st]
+    grads = [host_u16(x[k]) for x in reps]
+    gpu.sharded_adam_step(plan, reps, gpu.LOCAL, w.scale, *st, par, gpu.LOCAL, **hp_kwargs(w.hp, 1))
+    torch.cuda.synchronize()
+    want_par = np.zeros(k.numel(), np.uint16)
+    ON.step(grads, w.scale, *before, ON.hp_array(w.hp, 1), want_par)
+    for got, want, nm in zip(st, before, ("master", "exp_avg", "exp_avg_sq")):
+        assert_f32(host_f32(got[k]), want, f"{name} {nm}")
+    assert_bf16(host_u16(par[k]), want_par, f"{name} params")
+    # every slot is owned here, and every one was written (no sentinel left;
+    # the sentinel is a NaN pattern, which no updated parameter is)
+    assert plan.owned_numel == Ln
+    assert int((par == SENTINEL).sum()) == 0
+    del slices, reps, st, par
+    free()

@@ -1,0 +1,369 @@
+// The C-ABI of libzdo: argument checks, the host-side Adam constants and the
+// launches. Declared and documented in include/zdo.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <new>
+#include <string>
+
+#include "kernels.h"
+#include "zdo_internal.h"
+
+namespace zdo {
+
+int build_plan(const int64_t *param_numel, int32_t n_params, int64_t bucket_numel, int32_t dp_size,
+               int32_t rank, zdo_plan &p);
+int upload_plan(zdo_plan &p);
+
+namespace {
+
+thread_local std::string g_error;
+
+struct Span {
+    uintptr_t lo, hi;
+};
+
+Span span_of(const void *p, int64_t elems, int64_t elem_bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return {lo, lo + uintptr_t(elems) * uintptr_t(elem_bytes)};
+}
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.hi && b.lo < b.hi; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int fail(int code, const std::string &msg) {
+    g_error = msg;
+    return code;
+}
+
+// The plan must be device-ready, and on the current device.
+int check_plan(const zdo_plan *plan, const char *fn) {
+    if (!plan)
+        return fail(ZDO_EINVAL, std::string(fn) + ": plan is NULL");
+    if (!plan->d_table)
+        return fail(ZDO_EHIP, std::string(fn) + ": the plan has no device table (no HIP device when it was built)");
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return fail(ZDO_EHIP, std::string(fn) + ": hipGetDevice failed");
+    if (dev != plan->device)
+        return fail(ZDO_EINVAL, std::string(fn) + ": the plan was built on device " + std::to_string(plan->device) +
+                                    " but device " + std::to_string(dev) + " is current");
+    return ZDO_OK;
+}
+
+int check_coords(int32_t c, const char *fn, const char *what) {
+    if (c != ZDO_WORLD && c != ZDO_LOCAL)
+        return fail(ZDO_EINVAL, std::string(fn) + ": " + what + " must be ZDO_WORLD or ZDO_LOCAL");
+    return ZDO_OK;
+}
+
+int check_ptr(const void *p, const char *fn, const char *what) {
+    if (!p)
+        return fail(ZDO_EINVAL, std::string(fn) + ": " + what + " is NULL");
+    if (!aligned16(p))
+        return fail(ZDO_EALIGN, std::string(fn) + ": " + what + " is not 16-byte aligned");
+    return ZDO_OK;
+}
+
+int64_t extent(const zdo_plan *p, int32_t coords) { return coords == ZDO_WORLD ? p->buffer_numel : p->shard_numel; }
+
+int launch_result(hipError_t e, const char *fn) {
+    if (e != hipSuccess)
+        return fail(ZDO_EHIP, std::string(fn) + ": launch failed: " + hipGetErrorString(e));
+    return ZDO_OK;
+}
+
+// Checks the replica list; fills `rep`.
+int take_replicas(const zdo_plan *p, const uint16_t *const *replicas, int32_t n, int32_t coords, const char *fn,
+                  const uint16_t *rep[ZDO_MAX_REPLICAS], Span spans[ZDO_MAX_REPLICAS]) {
+    if (!replicas)
+        return fail(ZDO_EINVAL, std::string(fn) + ": replica list is NULL");
+    for (int32_t j = 0; j < n; ++j) {
+        const std::string what = "replica " + std::to_string(j);
+        if (int rc = check_ptr(replicas[j], fn, what.c_str()))
+            return rc;
+        rep[j] = replicas[j];
+        spans[j] = span_of(replicas[j], extent(p, coords), 2);
+    }
+    return ZDO_OK;
+}
+
+// 1 - beta^t: the double 1.0 multiplied t times by (double)beta, rounded once
+// to fp32 (beta in [0, 1)). Once beta^t < 2^-60, 1 - beta^t is 1.0 in double
+// and stays so for every larger t, so the products stop there. The last
+// (beta, t, product) of a few betas is kept per thread, so that consecutive
+// steps cost O(1).
+float bias_correction(float beta, int64_t t) {
+    struct Entry {
+        float beta;
+        int64_t t;
+        double pw;
+    };
+    thread_local Entry cache[4] = {{-1.0f, 0, 1.0}, {-1.0f, 0, 1.0}, {-1.0f, 0, 1.0}, {-1.0f, 0, 1.0}};
+    thread_local unsigned next = 0;
+    Entry *e = nullptr;
+    for (auto &c : cache)
+        if (c.beta == beta && c.t <= t)
+            e = &c;
+    double pw = 1.0;
+    int64_t i = 0;
+    if (e) {
+        pw = e->pw;
+        i = e->t;
+    } else {
+        e = &cache[next++ % 4];
+    }
+    for (; i < t && pw >= 0x1p-60; ++i)
+        pw *= double(beta);
+    *e = {beta, t, pw};
+    return float(1.0 - pw);
+}
+
+}  // namespace
+
+void set_error(const std::string &msg) { g_error = msg; }
+
+}  // namespace zdo
+
+using namespace zdo;
+
+extern "C" {
+
+const char *zdo_last_error(void) { return g_error.c_str(); }
+
+int build_range_map(const int64_t *param_numel, int32_t n_params, int64_t bucket_numel, int32_t dp_size,
+                    int32_t rank, zdo_plan **out) {
+    if (!out)
+        return fail(ZDO_EINVAL, "build_range_map: out is NULL");
+    *out = nullptr;
+    zdo_plan *p = new (std::nothrow) zdo_plan();
+    if (!p)
+        return fail(ZDO_ENOMEM, "build_range_map: out of host memory");
+    int rc;
+    try {
+        rc = build_plan(param_numel, n_params, bucket_numel, dp_size, rank, *p);
+        if (rc == ZDO_OK)
+            rc = upload_plan(*p);
+    } catch (const std::bad_alloc &) {
+        rc = fail(ZDO_ENOMEM, "build_range_map: out of host memory");
+    }
+    if (rc != ZDO_OK) {
+        zdo_plan_destroy(p);
+        return rc;
+    }
+    *out = p;
+    return ZDO_OK;
+}
+
+void zdo_plan_destroy(zdo_plan *plan) {
+    if (!plan)
+        return;
+    if (plan->d_table)
+        (void)hipFree(plan->d_table);
+    delete plan;
+}
+
+int64_t zdo_plan_buffer_numel(const zdo_plan *p) { return p ? p->buffer_numel : -1; }
+int64_t zdo_plan_shard_numel(const zdo_plan *p) { return p ? p->shard_numel : -1; }
+int64_t zdo_plan_owned_numel(const zdo_plan *p) { return p ? p->owned_numel : -1; }
+int32_t zdo_plan_dp_size(const zdo_plan *p) { return p ? p->dp_size : -1; }
+int32_t zdo_plan_rank(const zdo_plan *p) { return p ? p->rank : -1; }
+
+int zdo_plan_buckets(const zdo_plan *p, zdo_bucket *out, int32_t cap, int32_t *n) {
+    if (!p || !n)
+        return fail(ZDO_EINVAL, "zdo_plan_buckets: plan or n is NULL");
+    *n = int32_t(p->buckets.size());
+    if (out && cap >= *n)
+        for (int32_t i = 0; i < *n; ++i)
+            out[i] = p->buckets[size_t(i)];
+    return ZDO_OK;
+}
+
+int zdo_plan_pieces(const zdo_plan *p, zdo_piece *out, int64_t cap, int64_t *n) {
+    if (!p || !n)
+        return fail(ZDO_EINVAL, "zdo_plan_pieces: plan or n is NULL");
+    *n = int64_t(p->pieces.size());
+    if (out && cap >= *n)
+        for (int64_t i = 0; i < *n; ++i)
+            out[i] = p->pieces[size_t(i)];
+    return ZDO_OK;
+}
+
+int reduce_scatter_local(const zdo_plan *plan, const uint16_t *const *replicas, int32_t n_replicas,
+                         int32_t replica_coords, float scale, uint16_t *out, int32_t out_coords, void *stream) {
+    const char *fn = "reduce_scatter_local";
+    if (int rc = check_plan(plan, fn))
+        return rc;
+    if (n_replicas != plan->dp_size)
+        return fail(ZDO_EINVAL, std::string(fn) + ": n_replicas must equal the DP size " +
+                                    std::to_string(plan->dp_size));
+    if (int rc = check_coords(replica_coords, fn, "replica_coords"))
+        return rc;
+    if (int rc = check_coords(out_coords, fn, "out_coords"))
+        return rc;
+    ReduceArgs a{};
+    Span spans[ZDO_MAX_REPLICAS];
+    if (int rc = take_replicas(plan, replicas, n_replicas, replica_coords, fn, a.rep, spans))
+        return rc;
+    if (int rc = check_ptr(out, fn, "out"))
+        return rc;
+    const Span so = span_of(out, extent(plan, out_coords), 2);
+    for (int32_t j = 0; j < n_replicas; ++j)
+        if (overlap(so, spans[j]) && !(out == replicas[j] && out_coords == replica_coords))
+            return fail(ZDO_EALIAS, std::string(fn) + ": out overlaps replica " + std::to_string(j) +
+                                        " without coinciding with it");
+    a.walk = {plan->d_range_segs, plan->d_range_tile_seg, plan->range_tiles, 0};
+    a.nrep = n_replicas;
+    a.in_local = replica_coords == ZDO_LOCAL;
+    a.out_local = out_coords == ZDO_LOCAL;
+    a.scale = scale;
+    a.out = out;
+    return launch_result(launch_reduce(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int force_all_reduce(const zdo_plan *plan, const uint16_t *const *replicas, int32_t n_replicas, float scale,
+                     uint16_t *out_full, void *stream) {
+    const char *fn = "force_all_reduce";
+    if (int rc = check_plan(plan, fn))
+        return rc;
+    if (n_replicas != plan->dp_size)
+        return fail(ZDO_EINVAL, std::string(fn) + ": n_replicas must equal the DP size " +
+                                    std::to_string(plan->dp_size));
+    ReduceArgs a{};
+    Span spans[ZDO_MAX_REPLICAS];
+    if (int rc = take_replicas(plan, replicas, n_replicas, ZDO_WORLD, fn, a.rep, spans))
+        return rc;
+    if (int rc = check_ptr(out_full, fn, "out_full"))
+        return rc;
+    const Span so = span_of(out_full, plan->buffer_numel, 2);
+    for (int32_t j = 0; j < n_replicas; ++j)
+        if (overlap(so, spans[j]) && out_full != replicas[j])
+            return fail(ZDO_EALIAS, std::string(fn) + ": out_full overlaps replica " + std::to_string(j) +
+                                        " without coinciding with it");
+    a.walk = {nullptr, nullptr, seg_tiles(0, plan->buffer_numel), plan->buffer_numel};
+    a.nrep = n_replicas;
+    a.in_local = 0;
+    a.out_local = 0;
+    a.scale = scale;
+    a.out = out_full;
+    return launch_result(launch_reduce(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int sharded_adam_step(const zdo_plan *plan, const uint16_t *const *grads, int32_t n_grads, int32_t grad_coords,
+                      float scale, float *master, float *exp_avg, float *exp_avg_sq, uint16_t *param_out,
+                      int32_t param_coords, const zdo_adam *hp, float *main_grad_out, void *stream) {
+    const char *fn = "sharded_adam_step";
+    if (int rc = check_plan(plan, fn))
+        return rc;
+    if (n_grads != plan->dp_size && n_grads != 1)
+        return fail(ZDO_EINVAL, std::string(fn) + ": n_grads must be the DP size " + std::to_string(plan->dp_size) +
+                                    " or 1 (pre-reduced)");
+    if (int rc = check_coords(grad_coords, fn, "grad_coords"))
+        return rc;
+    if (param_out)
+        if (int rc = check_coords(param_coords, fn, "param_coords"))
+            return rc;
+    if (!hp)
+        return fail(ZDO_EINVAL, std::string(fn) + ": hp is NULL");
+    if (hp->step < 1 || hp->reserved != 0)
+        return fail(ZDO_EINVAL, std::string(fn) + ": hp->step must be >= 1 and hp->reserved 0");
+    if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f && hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
+        return fail(ZDO_EINVAL, std::string(fn) + ": beta1 and beta2 must be in [0, 1)");
+    StepArgs a{};
+    Span gs[ZDO_MAX_REPLICAS];
+    if (int rc = take_replicas(plan, grads, n_grads, grad_coords, fn, a.rep, gs))
+        return rc;
+    if (int rc = check_ptr(master, fn, "master"))
+        return rc;
+    if (int rc = check_ptr(exp_avg, fn, "exp_avg"))
+        return rc;
+    if (int rc = check_ptr(exp_avg_sq, fn, "exp_avg_sq"))
+        return rc;
+    if (param_out)
+        if (int rc = check_ptr(param_out, fn, "param_out"))
+            return rc;
+    if (main_grad_out)
+        if (int rc = check_ptr(main_grad_out, fn, "main_grad_out"))
+            return rc;
+    const int64_t L = plan->shard_numel;
+    // Every written buffer must be disjoint from every other buffer.
+    struct Named {
+        Span s;
+        const char *name;
+    };
+    Named written[5];
+    int nw = 0;
+    written[nw++] = {span_of(master, L, 4), "master"};
+    written[nw++] = {span_of(exp_avg, L, 4), "exp_avg"};
+    written[nw++] = {span_of(exp_avg_sq, L, 4), "exp_avg_sq"};
+    if (param_out)
+        written[nw++] = {span_of(param_out, extent(plan, param_coords), 2), "param_out"};
+    if (main_grad_out)
+        written[nw++] = {span_of(main_grad_out, L, 4), "main_grad_out"};
+    for (int i = 0; i < nw; ++i) {
+        for (int k = i + 1; k < nw; ++k)
+            if (overlap(written[i].s, written[k].s))
+                return fail(ZDO_EALIAS, std::string(fn) + ": " + written[i].name + " overlaps " + written[k].name);
+        for (int32_t j = 0; j < n_grads; ++j)
+            if (overlap(written[i].s, gs[j]))
+                return fail(ZDO_EALIAS, std::string(fn) + ": " + written[i].name + " overlaps grad " +
+                                            std::to_string(j));
+    }
+    a.walk = {plan->d_param_segs, plan->d_param_tile_seg, plan->param_tiles, 0};
+    a.nrep = n_grads;
+    a.in_local = grad_coords == ZDO_LOCAL;
+    a.param_local = param_coords == ZDO_LOCAL;
+    a.scale = scale;
+    a.master = master;
+    a.m = exp_avg;
+    a.v = exp_avg_sq;
+    a.param = param_out;
+    a.main_grad = main_grad_out;
+    a.c.lr = hp->lr;
+    a.c.b1 = hp->beta1;
+    a.c.b2 = hp->beta2;
+    a.c.omb1 = 1.0f - hp->beta1;
+    a.c.omb2 = 1.0f - hp->beta2;
+    a.c.eps = hp->eps;
+    a.c.wd = hp->weight_decay;
+    a.c.bc1 = bias_correction(hp->beta1, hp->step);
+    a.c.bc2 = bias_correction(hp->beta2, hp->step);
+    return launch_result(launch_step(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int writeback_params(const zdo_plan *plan, const float *master, uint16_t *param_out, int32_t param_coords,
+                     void *stream) {
+    const char *fn = "writeback_params";
+    if (int rc = check_plan(plan, fn))
+        return rc;
+    if (int rc = check_coords(param_coords, fn, "param_coords"))
+        return rc;
+    if (int rc = check_ptr(master, fn, "master"))
+        return rc;
+    if (int rc = check_ptr(param_out, fn, "param_out"))
+        return rc;
+    if (overlap(span_of(master, plan->shard_numel, 4), span_of(param_out, extent(plan, param_coords), 2)))
+        return fail(ZDO_EALIAS, std::string(fn) + ": param_out overlaps master");
+    WritebackArgs a{};
+    a.walk = {plan->d_param_segs, plan->d_param_tile_seg, plan->param_tiles, 0};
+    a.param_local = param_coords == ZDO_LOCAL;
+    a.master = master;
+    a.param = param_out;
+    return launch_result(launch_writeback(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int zdo_device_copy(void *dst, const void *src, int64_t bytes, void *stream) {
+    const char *fn = "zdo_device_copy";
+    if (bytes < 0 || bytes % 16 != 0)
+        return fail(ZDO_EINVAL, std::string(fn) + ": bytes must be a non-negative multiple of 16");
+    if (int rc = check_ptr(dst, fn, "dst"))
+        return rc;
+    if (int rc = check_ptr(src, fn, "src"))
+        return rc;
+    if (overlap(span_of(dst, bytes, 1), span_of(src, bytes, 1)))
+        return fail(ZDO_EALIAS, std::string(fn) + ": dst overlaps src");
+    return launch_result(launch_copy(dst, src, bytes / 16, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Launch arguments and launchers of the device kernels (kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "zdo_internal.h"
+
+namespace zdo {
+
+// Adam constants of one step, formed on the host (see abi.cpp).
+struct AdamConst {
+    float lr, b1, b2, omb1, omb2, eps, wd, bc1, bc2;
+};
+
+// Segments walked by a launch: either a table (segs + per-tile segment
+// index) or, when segs is NULL, the single run [0, flat_numel).
+struct Walk {
+    const Seg *segs;
+    const uint32_t *tile_seg;
+    int64_t ntiles;
+    int64_t flat_numel;
+};
+
+struct ReduceArgs {
+    Walk walk;
+    const uint16_t *rep[ZDO_MAX_REPLICAS];
+    int32_t nrep;
+    int32_t in_local;    // replicas indexed by LOCAL (1) or WORLD (0) position
+    int32_t out_local;
+    float scale;
+    uint16_t *out;
+};
+
+struct StepArgs {
+    Walk walk;
+    const uint16_t *rep[ZDO_MAX_REPLICAS];
+    int32_t nrep;
+    int32_t in_local;
+    int32_t param_local;
+    float scale;
+    float *master, *m, *v;
+    uint16_t *param;     // may be NULL
+    float *main_grad;    // may be NULL
+    AdamConst c;
+};
+
+struct WritebackArgs {
+    Walk walk;
+    int32_t param_local;
+    const float *master;
+    uint16_t *param;
+};
+
+hipError_t launch_reduce(const ReduceArgs &a, hipStream_t stream);
+hipError_t launch_step(const StepArgs &a, hipStream_t stream);
+hipError_t launch_writeback(const WritebackArgs &a, hipStream_t stream);
+hipError_t launch_copy(void *dst, const void *src, int64_t n16, hipStream_t stream);
+
+}  // namespace zdo

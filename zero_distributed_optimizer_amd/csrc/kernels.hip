@@ -1,0 +1,334 @@
+// Device kernels for gfx950 (CDNA4): the fused sharded Adam step, the
+// reduce-scatter / all-reduce of the D contributions, the parameter
+// write-back and a plain copy.
+//
+// The step is a pure stream over the rank's elements: (2D + 26) bytes per
+// element against a few dozen VALU operations, so it is bound by HBM
+// bandwidth, not by the matrix cores. The layout makes every stream
+// 16-byte-phase-aligned together (a LOCAL index is congruent to its WORLD
+// index modulo 8), so one lane takes an 8-element chunk: one 16-byte load per
+// replica, two per fp32 state array. A 256-thread block takes a tile of 256
+// consecutive chunks of one segment; a wave covers 1 KiB of every replica
+// and 2 KiB of every state array, contiguously. The chunks cut by a segment's
+// ends take a per-element path.
+//
+// Arithmetic is fixed (contraction off, IEEE division and square root,
+// fp32 subnormals kept) so that results match a sequential CPU evaluation bit
+// for bit; the order of operations is the one stated in include/zdo.h.
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+#pragma clang fp contract(off)
+
+namespace zdo {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ---- bf16 ----------------------------------------------------------------------
+// A bf16 is the top half of an fp32: widening is a shift or a mask.
+__device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float h_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// Two fp32 to their nearest bf16 (ties to even), packed a | b << 16: one
+// v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t to_bf16x2(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// ---- memory ------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 ld16(const uint16_t *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+__device__ __forceinline__ f32x4 ldf4(const float *p) {
+    return *reinterpret_cast<const f32x4 *>(p);
+}
+__device__ __forceinline__ void st16(uint16_t *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+__device__ __forceinline__ void stf4(float *p, f32x4 v) { *reinterpret_cast<f32x4 *>(p) = v; }
+
+// ---- walking the segments -------------------------------------------------------------
+struct ChunkPos {
+    int64_t w0;     // WORLD index of the chunk's first slot (a multiple of 8)
+    int64_t k0;     // LOCAL index of the same slot
+    int lo, hi;     // the chunk's slots [lo, hi) that belong to the segment
+};
+
+// The chunk this thread takes in `tile`; false if the tile ends before it.
+__device__ __forceinline__ bool chunk_of(const Walk &wk, int64_t tile, ChunkPos &c) {
+    int64_t wbeg, lbeg, len, tile0;
+    if (wk.segs) {
+        const Seg *s = wk.segs + wk.tile_seg[tile];
+        wbeg = s->wbeg;
+        lbeg = s->lbeg;
+        len = s->len;
+        tile0 = s->tile0;
+    } else {
+        wbeg = 0;
+        lbeg = 0;
+        len = wk.flat_numel;
+        tile0 = 0;
+    }
+    const int64_t q0 = wbeg / kChunk;
+    const int64_t w0 = (q0 + (tile - tile0) * kBlock + threadIdx.x) * kChunk;
+    const int64_t wend = wbeg + len;
+    if (w0 >= wend)
+        return false;
+    c.w0 = w0;
+    c.k0 = lbeg - (wbeg - q0 * kChunk) + (w0 - q0 * kChunk);
+    c.lo = w0 < wbeg ? int(wbeg - w0) : 0;
+    c.hi = w0 + kChunk > wend ? int(wend - w0) : kChunk;
+    return true;
+}
+
+// ---- the reduction ------------------------------------------------------------------------
+// s_j = bf16(g_j * scale); acc = s_0 + s_1 + ... in rank order (fp32).
+__device__ __forceinline__ void first_term(float acc[8], u32x4 r, float scale) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t s = to_bf16x2(lo_f32(r[k]) * scale, hi_f32(r[k]) * scale);
+        acc[2 * k] = lo_f32(s);
+        acc[2 * k + 1] = hi_f32(s);
+    }
+}
+__device__ __forceinline__ void add_term(float acc[8], u32x4 r, float scale) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t s = to_bf16x2(lo_f32(r[k]) * scale, hi_f32(r[k]) * scale);
+        acc[2 * k] = acc[2 * k] + lo_f32(s);
+        acc[2 * k + 1] = acc[2 * k + 1] + hi_f32(s);
+    }
+}
+
+// Sum of the contributions over one full chunk at index `gi` of every replica.
+template <int D>
+__device__ __forceinline__ void reduce_chunk(const uint16_t *const *rep, int nrep, int64_t gi, float scale,
+                                             float acc[8]) {
+    if constexpr (D > 0) {
+        u32x4 r[D];
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            r[j] = ld16(rep[j] + gi);
+        first_term(acc, r[0], scale);
+#pragma unroll
+        for (int j = 1; j < D; ++j)
+            add_term(acc, r[j], scale);
+    } else {
+        first_term(acc, ld16(rep[0] + gi), scale);
+        for (int j = 1; j < nrep; ++j)
+            add_term(acc, ld16(rep[j] + gi), scale);
+    }
+}
+
+// The same for one element.
+template <int D>
+__device__ __forceinline__ float reduce_one(const uint16_t *const *rep, int nrep, int64_t i, float scale) {
+    const int n = D > 0 ? D : nrep;
+    float acc = lo_f32(to_bf16x2(h_f32(rep[0][i]) * scale, 0.0f));
+    for (int j = 1; j < n; ++j)
+        acc = acc + lo_f32(to_bf16x2(h_f32(rep[j][i]) * scale, 0.0f));
+    return acc;
+}
+
+// ---- Adam --------------------------------------------------------------------------------------
+__device__ __forceinline__ void adam(const AdamConst &c, float g, float &p, float &m, float &v) {
+    const float m1 = c.b1 * m;
+    const float m2 = c.omb1 * g;
+    const float mn = m1 + m2;
+    const float gg = g * g;
+    const float v1 = c.b2 * v;
+    const float v2 = c.omb2 * gg;
+    const float vn = v1 + v2;
+    const float mh = mn / c.bc1;
+    const float vh = vn / c.bc2;
+    const float den = __builtin_sqrtf(vh) + c.eps;
+    const float u = mh / den;
+    const float wdp = c.wd * p;
+    const float u2 = u + wdp;
+    const float st = c.lr * u2;
+    p = p - st;
+    m = mn;
+    v = vn;
+}
+
+// ---- kernels -------------------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceArgs a) {
+    for (int64_t tile = blockIdx.x; tile < a.walk.ntiles; tile += gridDim.x) {
+        ChunkPos c;
+        if (!chunk_of(a.walk, tile, c))
+            continue;
+        const int64_t gi = a.in_local ? c.k0 : c.w0;
+        const int64_t oi = a.out_local ? c.k0 : c.w0;
+        if (c.lo == 0 && c.hi == kChunk) {
+            float acc[8];
+            reduce_chunk<D>(a.rep, a.nrep, gi, a.scale, acc);
+            u32x4 o;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                o[k] = to_bf16x2(acc[2 * k], acc[2 * k + 1]);
+            st16(a.out + oi, o);
+        } else {
+            for (int e = c.lo; e < c.hi; ++e) {
+                const float acc = reduce_one<D>(a.rep, a.nrep, gi + e, a.scale);
+                a.out[oi + e] = uint16_t(to_bf16x2(acc, 0.0f));
+            }
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a) {
+    for (int64_t tile = blockIdx.x; tile < a.walk.ntiles; tile += gridDim.x) {
+        ChunkPos c;
+        if (!chunk_of(a.walk, tile, c))
+            continue;
+        const int64_t gi = a.in_local ? c.k0 : c.w0;
+        const int64_t pi = a.param_local ? c.k0 : c.w0;
+        const int64_t k0 = c.k0;
+        if (c.lo == 0 && c.hi == kChunk) {
+            float acc[8];
+            reduce_chunk<D>(a.rep, a.nrep, gi, a.scale, acc);
+            float g[8], p[8], m[8], v[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t r = to_bf16x2(acc[2 * k], acc[2 * k + 1]);
+                g[2 * k] = lo_f32(r);
+                g[2 * k + 1] = hi_f32(r);
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const f32x4 pv = ldf4(a.master + k0 + 4 * h);
+                const f32x4 mv = ldf4(a.m + k0 + 4 * h);
+                const f32x4 vv = ldf4(a.v + k0 + 4 * h);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    p[4 * h + e] = pv[e];
+                    m[4 * h + e] = mv[e];
+                    v[4 * h + e] = vv[e];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                adam(a.c, g[e], p[e], m[e], v[e]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                stf4(a.master + k0 + 4 * h, f32x4{p[4 * h], p[4 * h + 1], p[4 * h + 2], p[4 * h + 3]});
+                stf4(a.m + k0 + 4 * h, f32x4{m[4 * h], m[4 * h + 1], m[4 * h + 2], m[4 * h + 3]});
+                stf4(a.v + k0 + 4 * h, f32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]});
+                if (a.main_grad)
+                    stf4(a.main_grad + k0 + 4 * h, f32x4{g[4 * h], g[4 * h + 1], g[4 * h + 2], g[4 * h + 3]});
+            }
+            if (a.param) {
+                u32x4 o;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    o[k] = to_bf16x2(p[2 * k], p[2 * k + 1]);
+                st16(a.param + pi, o);
+            }
+        } else {
+            for (int e = c.lo; e < c.hi; ++e) {
+                const float acc = reduce_one<D>(a.rep, a.nrep, gi + e, a.scale);
+                const float g = lo_f32(to_bf16x2(acc, 0.0f));
+                float p = a.master[k0 + e], m = a.m[k0 + e], v = a.v[k0 + e];
+                adam(a.c, g, p, m, v);
+                a.master[k0 + e] = p;
+                a.m[k0 + e] = m;
+                a.v[k0 + e] = v;
+                if (a.main_grad)
+                    a.main_grad[k0 + e] = g;
+                if (a.param)
+                    a.param[pi + e] = uint16_t(to_bf16x2(p, 0.0f));
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void writeback_kernel(WritebackArgs a) {
+    for (int64_t tile = blockIdx.x; tile < a.walk.ntiles; tile += gridDim.x) {
+        ChunkPos c;
+        if (!chunk_of(a.walk, tile, c))
+            continue;
+        const int64_t pi = a.param_local ? c.k0 : c.w0;
+        if (c.lo == 0 && c.hi == kChunk) {
+            const f32x4 x0 = ldf4(a.master + c.k0), x1 = ldf4(a.master + c.k0 + 4);
+            u32x4 o = {to_bf16x2(x0[0], x0[1]), to_bf16x2(x0[2], x0[3]), to_bf16x2(x1[0], x1[1]),
+                       to_bf16x2(x1[2], x1[3])};
+            st16(a.param + pi, o);
+        } else {
+            for (int e = c.lo; e < c.hi; ++e)
+                a.param[pi + e] = uint16_t(to_bf16x2(a.master[c.k0 + e], 0.0f));
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void copy_kernel(u32x4 *dst, const u32x4 *src, int64_t n16) {
+    for (int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x; i < n16; i += int64_t(gridDim.x) * kBlock)
+        dst[i] = src[i];
+}
+
+// Enough blocks to cover every tile once, up to a cap that keeps the grid's
+// work-item count in range; larger launches loop over tiles.
+constexpr int64_t kMaxGrid = int64_t(1) << 22;
+
+unsigned grid_for(int64_t ntiles) {
+    return unsigned(ntiles < kMaxGrid ? ntiles : kMaxGrid);
+}
+
+}  // namespace
+
+hipError_t launch_reduce(const ReduceArgs &a, hipStream_t stream) {
+    if (a.walk.ntiles <= 0)
+        return hipSuccess;
+    const dim3 grid(grid_for(a.walk.ntiles)), block(kBlock);
+    switch (a.nrep) {
+    case 1: hipLaunchKernelGGL(reduce_kernel<1>, grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(reduce_kernel<2>, grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(reduce_kernel<4>, grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(reduce_kernel<8>, grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL(reduce_kernel<16>, grid, block, 0, stream, a); break;
+    case 32: hipLaunchKernelGGL(reduce_kernel<32>, grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL(reduce_kernel<0>, grid, block, 0, stream, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_step(const StepArgs &a, hipStream_t stream) {
+    if (a.walk.ntiles <= 0)
+        return hipSuccess;
+    const dim3 grid(grid_for(a.walk.ntiles)), block(kBlock);
+    switch (a.nrep) {
+    case 1: hipLaunchKernelGGL(step_kernel<1>, grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(step_kernel<2>, grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(step_kernel<4>, grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(step_kernel<8>, grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL(step_kernel<16>, grid, block, 0, stream, a); break;
+    case 32: hipLaunchKernelGGL(step_kernel<32>, grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL(step_kernel<0>, grid, block, 0, stream, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_writeback(const WritebackArgs &a, hipStream_t stream) {
+    if (a.walk.ntiles <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(writeback_kernel, dim3(grid_for(a.walk.ntiles)), dim3(kBlock), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy(void *dst, const void *src, int64_t n16, hipStream_t stream) {
+    if (n16 <= 0)
+        return hipSuccess;
+    const int64_t blocks = (n16 + kBlock - 1) / kBlock;
+    hipLaunchKernelGGL(copy_kernel, dim3(grid_for(blocks)), dim3(kBlock), 0, stream, static_cast<u32x4 *>(dst),
+                       static_cast<const u32x4 *>(src), n16);
+    return hipGetLastError();
+}
+
+}  // namespace zdo

@@ -1,0 +1,184 @@
+// Host side of the plan: bucket layout, rank ranges, the four-way range map
+// and the segment table the kernels walk.
+//
+// Page "04 · 分布式优化器": one flat buffer cut into buckets by size (§2), each
+// padded to a multiple of the DP size by the layout (§5) and split into D
+// equal contiguous ranges, rank r owning range r (§2, §3); per parameter
+// piece, the four ranges gbuf_world, gbuf_world_in_bucket, gbuf_local and
+// param, translations of one another (§4.1).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <new>
+
+#include "zdo_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxNumel = int64_t(1) << 56;
+
+int64_t floor_mod(int64_t a, int64_t m) {
+    int64_t r = a % m;
+    return r < 0 ? r + m : r;
+}
+
+}  // namespace
+
+namespace zdo {
+
+int build_plan(const int64_t *param_numel, int32_t n_params, int64_t bucket_numel, int32_t dp_size,
+               int32_t rank, zdo_plan &p) {
+    if (!param_numel || n_params < 1) {
+        set_error("build_range_map: need at least one parameter");
+        return ZDO_EINVAL;
+    }
+    if (bucket_numel < 1) {
+        set_error("build_range_map: bucket_numel must be >= 1");
+        return ZDO_EINVAL;
+    }
+    if (dp_size < 1 || dp_size > ZDO_MAX_REPLICAS) {
+        set_error("build_range_map: dp_size must be in [1, " + std::to_string(ZDO_MAX_REPLICAS) + "]");
+        return ZDO_EINVAL;
+    }
+    if (rank < 0 || rank >= dp_size) {
+        set_error("build_range_map: rank must be in [0, dp_size)");
+        return ZDO_EINVAL;
+    }
+    p.dp_size = dp_size;
+    p.rank = rank;
+    p.bucket_numel = bucket_numel;
+    p.param_numel.assign(param_numel, param_numel + n_params);
+
+    // Buckets: parameters in order, packed; a bucket closes right after the
+    // parameter that brings it to bucket_numel elements or after the last one,
+    // and is padded at its tail to a multiple of D.
+    std::vector<int64_t> param_start(n_params);
+    std::vector<int32_t> param_bucket(n_params);
+    int64_t offset = 0, filled = 0;
+    for (int32_t i = 0; i < n_params; ++i) {
+        const int64_t n = param_numel[i];
+        if (n < 1 || n > kMaxNumel) {
+            set_error("build_range_map: parameter " + std::to_string(i) + " has a bad element count");
+            return ZDO_EINVAL;
+        }
+        param_start[i] = offset + filled;
+        param_bucket[i] = int32_t(p.buckets.size());
+        filled += n;
+        if (offset + filled > kMaxNumel) {
+            set_error("build_range_map: buffer too large");
+            return ZDO_EINVAL;
+        }
+        if (filled >= bucket_numel || i == n_params - 1) {
+            zdo_bucket b{};
+            b.offset = offset;
+            b.numel = filled;
+            b.padded_numel = (filled + dp_size - 1) / dp_size * dp_size;
+            b.shard_numel = b.padded_numel / dp_size;
+            p.buckets.push_back(b);
+            offset += b.padded_numel;
+            filled = 0;
+        }
+    }
+    p.buffer_numel = offset;
+
+    // The rank's shard: per bucket, the local view starts at the first slot
+    // at or after the previous view's end that has the WORLD start's phase
+    // modulo 8.
+    int64_t end = 0;
+    for (auto &b : p.buckets) {
+        const int64_t rstart = b.offset + int64_t(rank) * b.shard_numel;
+        b.shard_base = end + floor_mod(rstart - end, kChunk);
+        end = b.shard_base + b.shard_numel;
+    }
+    p.shard_numel = end;
+
+    // Pieces: every parameter's overlap with the rank's range of its bucket.
+    int32_t i = 0;
+    for (int32_t bi = 0; bi < int32_t(p.buckets.size()); ++bi) {
+        const zdo_bucket &b = p.buckets[bi];
+        const int64_t rs = b.offset + int64_t(rank) * b.shard_numel;
+        const int64_t re = rs + b.shard_numel;
+        for (; i < n_params && param_bucket[i] == bi; ++i) {
+            const int64_t ps = param_start[i], pe = ps + param_numel[i];
+            const int64_t lo = std::max(ps, rs), hi = std::min(pe, re);
+            if (lo >= hi)
+                continue;
+            zdo_piece pc{};
+            pc.param_index = i;
+            pc.bucket_index = bi;
+            pc.gbuf_world = {lo, hi};
+            pc.gbuf_world_in_bucket = {lo - b.offset, hi - b.offset};
+            pc.gbuf_local = {lo - rs, hi - rs};
+            pc.param = {lo - ps, hi - ps};
+            pc.shard_offset = b.shard_base + (lo - rs);
+            p.pieces.push_back(pc);
+            p.owned_numel += hi - lo;
+        }
+        // Owned parameter elements of this bucket form one run (the padding
+        // sits at the bucket's tail); the whole range is one run as well.
+        const int64_t own_end = std::min(re, b.offset + b.numel);
+        if (own_end > rs)
+            p.param_segs.push_back({rs, b.shard_base, own_end - rs, 0});
+        p.range_segs.push_back({rs, b.shard_base, b.shard_numel, 0});
+    }
+    for (auto *segs : {&p.param_segs, &p.range_segs}) {
+        int64_t t = 0;
+        for (auto &s : *segs) {
+            s.tile0 = t;
+            t += seg_tiles(s.wbeg, s.len);
+        }
+        (segs == &p.param_segs ? p.param_tiles : p.range_tiles) = t;
+    }
+    return ZDO_OK;
+}
+
+int upload_plan(zdo_plan &p) {
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count < 1) {
+        (void)hipGetLastError();
+        return ZDO_OK;   // host-only plan
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        set_error("build_range_map: hipGetDevice failed");
+        return ZDO_EHIP;
+    }
+    // tile -> segment index of each launch space
+    std::vector<uint32_t> tile_seg;
+    tile_seg.reserve(size_t(p.param_tiles + p.range_tiles));
+    for (const auto *segs : {&p.param_segs, &p.range_segs})
+        for (size_t s = 0; s < segs->size(); ++s) {
+            const int64_t nt = seg_tiles((*segs)[s].wbeg, (*segs)[s].len);
+            tile_seg.insert(tile_seg.end(), size_t(nt), uint32_t(s));
+        }
+    const size_t nseg = p.param_segs.size() + p.range_segs.size();
+    const size_t seg_bytes = nseg * sizeof(Seg);
+    const size_t bytes = seg_bytes + tile_seg.size() * sizeof(uint32_t);
+    std::vector<char> host(bytes);
+    std::copy(p.param_segs.begin(), p.param_segs.end(), reinterpret_cast<Seg *>(host.data()));
+    std::copy(p.range_segs.begin(), p.range_segs.end(),
+              reinterpret_cast<Seg *>(host.data()) + p.param_segs.size());
+    std::copy(tile_seg.begin(), tile_seg.end(), reinterpret_cast<uint32_t *>(host.data() + seg_bytes));
+    void *d = nullptr;
+    hipError_t e = hipMalloc(&d, bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        set_error(std::string("build_range_map: hipMalloc of the segment table: ") + hipGetErrorString(e));
+        return e == hipErrorOutOfMemory ? ZDO_ENOMEM : ZDO_EHIP;
+    }
+    e = hipMemcpy(d, host.data(), bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(d);
+        set_error(std::string("build_range_map: upload of the segment table: ") + hipGetErrorString(e));
+        return ZDO_EHIP;
+    }
+    p.d_table = d;
+    p.d_param_segs = static_cast<const Seg *>(d);
+    p.d_range_segs = p.d_param_segs + p.param_segs.size();
+    p.d_param_tile_seg = reinterpret_cast<const uint32_t *>(static_cast<const char *>(d) + seg_bytes);
+    p.d_range_tile_seg = p.d_param_tile_seg + p.param_tiles;
+    p.device = dev;
+    return ZDO_OK;
+}
+
+}  // namespace zdo

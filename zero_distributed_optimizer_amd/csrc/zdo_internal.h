@@ -1,0 +1,58 @@
+// Internal declarations shared by the plan builder, the kernels and the C-ABI.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "zdo.h"
+
+namespace zdo {
+
+// A lane works on chunks of 8 consecutive elements: 16 bytes of bf16, 32 of fp32.
+constexpr int kChunk = 8;
+// Threads per block; a block takes one tile of kBlock chunks at a time.
+constexpr int kBlock = 256;
+constexpr int kTileElems = kChunk * kBlock;
+
+// One contiguous run of the rank's elements, as the kernels walk it.
+struct Seg {
+    int64_t wbeg;   // WORLD index of the first element
+    int64_t lbeg;   // LOCAL (shard) index of the first element; lbeg == wbeg (mod 8)
+    int64_t len;    // elements, >= 1
+    int64_t tile0;  // index of the segment's first tile in the launch's tile space
+};
+
+// Tiles a segment needs: its 8-element chunks (aligned to the WORLD index,
+// so a partial chunk at each end) in groups of kBlock.
+inline int64_t seg_chunks(int64_t wbeg, int64_t len) {
+    return (wbeg + len + kChunk - 1) / kChunk - wbeg / kChunk;
+}
+inline int64_t seg_tiles(int64_t wbeg, int64_t len) {
+    return (seg_chunks(wbeg, len) + kBlock - 1) / kBlock;
+}
+
+void set_error(const std::string &msg);
+
+}  // namespace zdo
+
+struct zdo_plan {
+    int32_t dp_size = 0, rank = 0;
+    int64_t bucket_numel = 0;
+    std::vector<int64_t> param_numel;
+    std::vector<zdo_bucket> buckets;
+    std::vector<zdo_piece> pieces;
+    int64_t buffer_numel = 0;  // N
+    int64_t shard_numel = 0;   // L
+    int64_t owned_numel = 0;   // E
+    // Owned parameter elements (one run per bucket, padding excluded) and the
+    // rank's whole range of every bucket (padding included).
+    std::vector<zdo::Seg> param_segs, range_segs;
+    int64_t param_tiles = 0, range_tiles = 0;
+    // Device copies, in one allocation on `device`: both segment lists and,
+    // for every tile of each launch space, the index of its segment.
+    void *d_table = nullptr;
+    const zdo::Seg *d_param_segs = nullptr, *d_range_segs = nullptr;
+    const uint32_t *d_param_tile_seg = nullptr, *d_range_tile_seg = nullptr;
+    int device = -1;
+};

@@ -219,7 +219,7 @@ int reduce_scatter_local(const zdo_plan *plan, const uint16_t *const *replicas, 
     a.out_local = out_coords == ZDO_LOCAL;
     a.scale = scale;
     a.out = out;
-    return launch_result(launch_reduce(a, static_cast<hipStream_t>(stream)), fn);
+    return launch_result(launch_reduce(a, plan->lds_per_cu, static_cast<hipStream_t>(stream)), fn);
 }
 
 int force_all_reduce(const zdo_plan *plan, const uint16_t *const *replicas, int32_t n_replicas, float scale,
@@ -247,7 +247,7 @@ int force_all_reduce(const zdo_plan *plan, const uint16_t *const *replicas, int3
     a.out_local = 0;
     a.scale = scale;
     a.out = out_full;
-    return launch_result(launch_reduce(a, static_cast<hipStream_t>(stream)), fn);
+    return launch_result(launch_reduce(a, plan->lds_per_cu, static_cast<hipStream_t>(stream)), fn);
 }
 
 int sharded_adam_step(const zdo_plan *plan, const uint16_t *const *grads, int32_t n_grads, int32_t grad_coords,
@@ -329,7 +329,7 @@ int sharded_adam_step(const zdo_plan *plan, const uint16_t *const *grads, int32_
     a.c.wd = hp->weight_decay;
     a.c.bc1 = bias_correction(hp->beta1, hp->step);
     a.c.bc2 = bias_correction(hp->beta2, hp->step);
-    return launch_result(launch_step(a, static_cast<hipStream_t>(stream)), fn);
+    return launch_result(launch_step(a, plan->lds_per_cu, static_cast<hipStream_t>(stream)), fn);
 }
 
 int writeback_params(const zdo_plan *plan, const float *master, uint16_t *param_out, int32_t param_coords,
@@ -350,7 +350,7 @@ int writeback_params(const zdo_plan *plan, const float *master, uint16_t *param_
     a.param_local = param_coords == ZDO_LOCAL;
     a.master = master;
     a.param = param_out;
-    return launch_result(launch_writeback(a, static_cast<hipStream_t>(stream)), fn);
+    return launch_result(launch_writeback(a, plan->lds_per_cu, static_cast<hipStream_t>(stream)), fn);
 }
 
 int zdo_device_copy(void *dst, const void *src, int64_t bytes, void *stream) {

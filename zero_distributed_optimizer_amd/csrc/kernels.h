@@ -51,9 +51,11 @@ struct WritebackArgs {
     uint16_t *param;
 };
 
-hipError_t launch_reduce(const ReduceArgs &a, hipStream_t stream);
-hipError_t launch_step(const StepArgs &a, hipStream_t stream);
-hipError_t launch_writeback(const WritebackArgs &a, hipStream_t stream);
+// lds_per_cu: LDS bytes per compute unit of the launch device (0 if unknown),
+// used to cap how many workgroups share a compute unit.
+hipError_t launch_reduce(const ReduceArgs &a, int lds_per_cu, hipStream_t stream);
+hipError_t launch_step(const StepArgs &a, int lds_per_cu, hipStream_t stream);
+hipError_t launch_writeback(const WritebackArgs &a, int lds_per_cu, hipStream_t stream);
 hipError_t launch_copy(void *dst, const void *src, int64_t n16, hipStream_t stream);
 
 }  // namespace zdo

@@ -178,6 +178,11 @@ int upload_plan(zdo_plan &p) {
     p.d_param_tile_seg = reinterpret_cast<const uint32_t *>(static_cast<const char *>(d) + seg_bytes);
     p.d_range_tile_seg = p.d_param_tile_seg + p.param_tiles;
     p.device = dev;
+    if (hipDeviceGetAttribute(&p.lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+        hipSuccess) {
+        (void)hipGetLastError();
+        p.lds_per_cu = 0;
+    }
     return ZDO_OK;
 }
 

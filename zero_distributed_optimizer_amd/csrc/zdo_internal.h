@@ -11,8 +11,11 @@ namespace zdo {
 
 // A lane works on chunks of 8 consecutive elements: 16 bytes of bf16, 32 of fp32.
 constexpr int kChunk = 8;
-// Threads per block; a block takes one tile of kBlock chunks at a time.
-constexpr int kBlock = 256;
+// Threads per workgroup; a workgroup takes one tile of kBlock chunks at a time.
+#ifndef ZDO_BLOCK
+#define ZDO_BLOCK 64
+#endif
+constexpr int kBlock = ZDO_BLOCK;
 constexpr int kTileElems = kChunk * kBlock;
 
 // One contiguous run of the rank's elements, as the kernels walk it.
@@ -55,4 +58,5 @@ struct zdo_plan {
     const zdo::Seg *d_param_segs = nullptr, *d_range_segs = nullptr;
     const uint32_t *d_param_tile_seg = nullptr, *d_range_tile_seg = nullptr;
     int device = -1;
+    int lds_per_cu = 0;   // bytes of LDS per compute unit on `device`
 };

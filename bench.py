@@ -67,6 +67,8 @@ def main() -> int:
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--stagger", type=int, default=0,
+                    help="extra bytes (a multiple of 16) placed between consecutive input buffers")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only: the D ranks' contributions are D "
@@ -93,18 +95,26 @@ def main() -> int:
     stride = (n_rep + 7) // 8 * 8
     log(f"workload {w.name}: N={N} D={D} rank={rank} E={E} L={Ln} grads={w.grad_mode}")
 
-    # inputs, resident in HBM before the timed region
+    # inputs, resident in HBM before the timed region: the D replicas in one
+    # allocation, then the three state arrays in another, each buffer
+    # `stagger` bytes further from the previous one than its size requires
+    if args.stagger % 16:
+        raise SystemExit("--stagger must be a multiple of 16")
     t0 = time.perf_counter()
-    rep_buf = torch.empty(D * stride, dtype=torch.bfloat16, device=dev)
+    gap2, gap4 = args.stagger // 2, args.stagger // 4
+    rep_buf = torch.empty(D * (stride + gap2), dtype=torch.bfloat16, device=dev)
     reps = []
     for j in range(D):
-        s = rep_buf[j * stride: j * stride + n_rep]
+        s = rep_buf[j * (stride + gap2): j * (stride + gap2) + n_rep]
         W.normal_bf16(n_rep, w.grad_sigma, W.seed(w.cfg, 0, "grad", j), out=s,
                       probe_fraction=w.probe_fraction, probe_seed=W.seed(w.cfg, 0, "probe", j))
         reps.append(s.view(torch.int16))
-    master = W.normal_f32(Ln, w.master_sigma, W.seed(w.cfg, 0, "master"), dev)
-    exp_avg = W.normal_f32(Ln, w.m_sigma, W.seed(w.cfg, 0, "m"), dev)
-    exp_avg_sq = W.square_normal_f32(Ln, w.v_sigma, W.seed(w.cfg, 0, "v"), dev)
+    sstride = (Ln + 3) // 4 * 4 + gap4
+    state_buf = torch.empty(3 * sstride, dtype=torch.float32, device=dev)
+    master, exp_avg, exp_avg_sq = (state_buf[i * sstride: i * sstride + Ln] for i in range(3))
+    W.normal_f32(Ln, w.master_sigma, W.seed(w.cfg, 0, "master"), out=master)
+    W.normal_f32(Ln, w.m_sigma, W.seed(w.cfg, 0, "m"), out=exp_avg)
+    W.square_normal_f32(Ln, w.v_sigma, W.seed(w.cfg, 0, "v"), out=exp_avg_sq)
     params = torch.zeros(n_rep, dtype=torch.int16, device=dev)
     torch.cuda.synchronize(dev)
     log(f"inputs generated in {time.perf_counter() - t0:.1f}s")
@@ -177,6 +187,8 @@ def main() -> int:
     log(f"cold caches: kernel avg {cold_s * 1e6:.1f} us, {cold['achieved_gbps']:.0f} GB/s algorithmic")
     del src, dst
 
+    variants = measure_variants(zdo, torch, np, plan, w, reps, coords, stream, min(args.steps, 50))
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(plan, w, reps, coords, master, exp_avg, exp_avg_sq, args.cpu_seconds)
@@ -207,6 +219,7 @@ def main() -> int:
             "grad_replicas": f"{D} x bf16 {'whole buffers' if coords == zdo.WORLD else 'shard slices'}",
             "state": "fp32 master/exp_avg/exp_avg_sq shard",
             "bytes_per_element": bytes_per_elem,
+            "buffer_stagger_bytes": args.stagger,
         },
         "hbm_gbps": alg_bytes / (ms_per_step / 1e3) / 1e9,
         "hbm_frac_of_peak": alg_bytes / (ms_per_step / 1e3) / 1e9 / PEAK_HBM_GBPS,
@@ -223,11 +236,51 @@ def main() -> int:
                    "p90_us": float(np.percentile(kern_ms, 90)) * 1e3,
                    "source_sha256_16": kernel_source_hash()},
         "cold_cache": cold,
+        "variants": variants,
         "copy_reference_gbps": copy_gbps,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> dict:
+    """The other two device calls on the same inputs: reduce_scatter_local over
+    the rank's whole ranges (2D + 2 bytes per element of the ranges) and, when
+    the replicas are whole buffers, force_all_reduce over the padded buffer
+    (2D + 2 bytes per buffer element). HIP events around each launch."""
+    D = plan.dp_size
+    out = {}
+
+    def timed(fn) -> float:
+        for _ in range(3):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+
+    ranges = int(sum(b["shard_numel"] for b in plan.buckets()))
+    red = torch.empty(plan.shard_numel, dtype=torch.int16, device=reps[0].device)
+    t = timed(lambda: zdo.reduce_scatter_local(plan, reps, coords, w.scale, red, zdo.LOCAL, stream))
+    gbps = ranges * (2 * D + 2) / t / 1e9
+    out["reduce_scatter_local"] = {"elements": ranges, "bytes_per_element": 2 * D + 2, "kernel_avg_us": t * 1e6,
+                                   "achieved_gbps": gbps, "frac": gbps / PEAK_HBM_GBPS}
+    log(f"reduce_scatter_local: {t * 1e6:.1f} us, {gbps:.0f} GB/s algorithmic")
+    del red
+    if coords == zdo.WORLD:
+        N = plan.buffer_numel
+        full = torch.empty(N, dtype=torch.int16, device=reps[0].device)
+        t = timed(lambda: zdo.force_all_reduce(plan, reps, w.scale, full, stream))
+        gbps = N * (2 * D + 2) / t / 1e9
+        out["force_all_reduce"] = {"elements": N, "bytes_per_element": 2 * D + 2, "kernel_avg_us": t * 1e6,
+                                   "achieved_gbps": gbps, "frac": gbps / PEAK_HBM_GBPS}
+        log(f"force_all_reduce: {t * 1e6:.1f} us, {gbps:.0f} GB/s algorithmic")
+        del full
+    return out
 
 
 def cpu_baseline(plan, w, reps, coords, master, exp_avg, exp_avg_sq, seconds: float) -> dict:

@@ -17,22 +17,27 @@ def lib():
     if _lib is None:
         if not os.path.exists(_build.LIB):
             _build.build()
-        L = ctypes.CDLL(_build.LIB)
-        i64, i32, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_float
-        vp = ctypes.c_void_p
-        L.oracle_bias_correction.argtypes = [f32, i64]
-        L.oracle_bias_correction.restype = f32
-        L.oracle_threads.argtypes = []
-        L.oracle_threads.restype = ctypes.c_int
-        L.oracle_narrow.argtypes = [vp, i64, vp]
-        L.oracle_widen.argtypes = [vp, i64, vp]
-        L.oracle_reduce.argtypes = [i32, vp, f32, i64, vp]
-        L.oracle_adam.argtypes = [i64, vp, vp, vp, vp, vp, vp]
-        L.oracle_step.argtypes = [i32, vp, f32, i64, vp, vp, vp, vp, vp, vp]
-        for f in (L.oracle_narrow, L.oracle_widen, L.oracle_reduce, L.oracle_adam, L.oracle_step):
-            f.restype = None
-        _lib = L
+        _lib = load(_build.LIB)
     return _lib
+
+
+def load(path: str):
+    """Load a build of oracle/step.c and declare its functions."""
+    L = ctypes.CDLL(path)
+    i64, i32, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    vp = ctypes.c_void_p
+    L.oracle_bias_correction.argtypes = [f32, i64]
+    L.oracle_bias_correction.restype = f32
+    L.oracle_threads.argtypes = []
+    L.oracle_threads.restype = ctypes.c_int
+    L.oracle_narrow.argtypes = [vp, i64, vp]
+    L.oracle_widen.argtypes = [vp, i64, vp]
+    L.oracle_reduce.argtypes = [i32, vp, f32, i64, vp]
+    L.oracle_adam.argtypes = [i64, vp, vp, vp, vp, vp, vp]
+    L.oracle_step.argtypes = [i32, vp, f32, i64, vp, vp, vp, vp, vp, vp]
+    for f in (L.oracle_narrow, L.oracle_widen, L.oracle_reduce, L.oracle_adam, L.oracle_step):
+        f.restype = None
+    return L
 
 
 def _ptr(a):

@@ -197,6 +197,13 @@ def test_reduce_order_is_fixed_rank_order():
     # the running sum starts from rank 0's term, so -0 + -0 stays -0
     nz = np.array([0x8000], np.uint16)
     assert S.all_reduce([nz, nz, nz], 1.0)[0] == 0x8000
+    # cancellation shows the order: 2^25 - 2^25 + 1 = 1 in rank order, while
+    # any order that adds the 1 to a +-2^25 first loses it to rounding
+    vals = [2.0**25, -2.0**25, 1.0]
+    reps = [torch_bf16_bits(np.array([x], np.float32)) for x in vals]
+    assert N.widen(S.all_reduce(reps, 1.0))[0] == 1.0
+    assert N.widen(S.all_reduce(reps[::-1], 1.0))[0] == 0.0
+    assert N.widen(S.all_reduce([reps[0], reps[2], reps[1]], 1.0))[0] == 0.0
 
 
 def test_scale_applied_before_reduce():

@@ -27,7 +27,7 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wextra", "-Wno-unused-parameter",
+    "-Wall", "-Wextra", "-Wno-unused-parameter", "-Wl,--no-undefined",
 ]
 
 

@@ -213,7 +213,7 @@ int reduce_scatter_local(const zdo_plan *plan, const uint16_t *const *replicas, 
         if (overlap(so, spans[j]) && !(out == replicas[j] && out_coords == replica_coords))
             return fail(ZDO_EALIAS, std::string(fn) + ": out overlaps replica " + std::to_string(j) +
                                         " without coinciding with it");
-    a.walk = {plan->d_range_segs, plan->d_range_tile_seg, plan->range_tiles, 0};
+    a.walk = {plan->d_range_segs, plan->d_range_tile_seg, plan->range_tiles, 0, int64_t(plan->range_segs.size())};
     a.nrep = n_replicas;
     a.in_local = replica_coords == ZDO_LOCAL;
     a.out_local = out_coords == ZDO_LOCAL;
@@ -241,7 +241,7 @@ int force_all_reduce(const zdo_plan *plan, const uint16_t *const *replicas, int3
         if (overlap(so, spans[j]) && out_full != replicas[j])
             return fail(ZDO_EALIAS, std::string(fn) + ": out_full overlaps replica " + std::to_string(j) +
                                         " without coinciding with it");
-    a.walk = {nullptr, nullptr, seg_tiles(0, plan->buffer_numel), plan->buffer_numel};
+    a.walk = {nullptr, nullptr, seg_tiles(0, plan->buffer_numel), plan->buffer_numel, 0};
     a.nrep = n_replicas;
     a.in_local = 0;
     a.out_local = 0;
@@ -310,7 +310,7 @@ int sharded_adam_step(const zdo_plan *plan, const uint16_t *const *grads, int32_
                 return fail(ZDO_EALIAS, std::string(fn) + ": " + written[i].name + " overlaps grad " +
                                             std::to_string(j));
     }
-    a.walk = {plan->d_param_segs, plan->d_param_tile_seg, plan->param_tiles, 0};
+    a.walk = {plan->d_param_segs, plan->d_param_tile_seg, plan->param_tiles, 0, int64_t(plan->param_segs.size())};
     a.nrep = n_grads;
     a.in_local = grad_coords == ZDO_LOCAL;
     a.param_local = param_coords == ZDO_LOCAL;
@@ -346,7 +346,7 @@ int writeback_params(const zdo_plan *plan, const float *master, uint16_t *param_
     if (overlap(span_of(master, plan->shard_numel, 4), span_of(param_out, extent(plan, param_coords), 2)))
         return fail(ZDO_EALIAS, std::string(fn) + ": param_out overlaps master");
     WritebackArgs a{};
-    a.walk = {plan->d_param_segs, plan->d_param_tile_seg, plan->param_tiles, 0};
+    a.walk = {plan->d_param_segs, plan->d_param_tile_seg, plan->param_tiles, 0, int64_t(plan->param_segs.size())};
     a.param_local = param_coords == ZDO_LOCAL;
     a.master = master;
     a.param = param_out;

@@ -19,6 +19,7 @@ struct Walk {
     const uint32_t *tile_seg;
     int64_t ntiles;
     int64_t flat_numel;
+    int64_t nseg;
 };
 
 struct ReduceArgs {

@@ -31,7 +31,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sharded Adam step: elements/s and HBM GB/s (% of peak) at 1 MI355X"
 PEAK_HBM_GBPS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "zero_distributed_optimizer_amd", "csrc", "kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "zero_distributed_optimizer_amd", "csrc", f)
+                  for f in ("kernels.hip", "kernels.h", "zdo_internal.h")]
 
 
 def log(msg: str) -> None:
@@ -39,8 +40,12 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] over the kernel source and the headers that shape it."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(workload: str) -> float | None:

@@ -34,7 +34,11 @@ def load(path: str):
     L.oracle_widen.argtypes = [vp, i64, vp]
     L.oracle_reduce.argtypes = [i32, vp, f32, i64, vp]
     L.oracle_adam.argtypes = [i64, vp, vp, vp, vp, vp, vp]
-    L.oracle_step.argtypes = [i32, vp, f32, i64, vp, vp, vp, vp, vp, vp]
+    L.oracle_step.argtypes = [i32, vp, f32, i64, vp, vp, vp, vp, vp, vp, f32]
+    L.oracle_norm_sq.argtypes = [i32, vp, f32, i64]
+    L.oracle_norm_sq.restype = ctypes.c_double
+    L.oracle_clip_coefficient.argtypes = [vp, i32, f32, vp]
+    L.oracle_clip_coefficient.restype = f32
     for f in (L.oracle_narrow, L.oracle_widen, L.oracle_reduce, L.oracle_adam, L.oracle_step):
         f.restype = None
     return L
@@ -114,7 +118,23 @@ def adam(grad, master, m, v, hp_arr, param_out=None) -> None:
     lib().oracle_adam(n, _ptr(grad), _ptr(master), _ptr(m), _ptr(v), _ptr(param_out), _ptr(hp_arr))
 
 
-def step(reps, scale: float, master, m, v, hp_arr, param_out=None, main_grad_out=None) -> None:
+def norm_sq(reps, scale: float) -> float:
+    """Sum of squares (fp64, element order) of the reduced gradient."""
+    n = reps[0].size
+    keep = list(reps)
+    return float(lib().oracle_norm_sq(len(keep), _rep_array(keep, n), scale, n))
+
+
+def clip_coefficient(parts, max_norm: float) -> tuple:
+    """(coefficient as fp32, global norm) from the ranks' squared norms."""
+    arr = np.ascontiguousarray(np.asarray(parts, dtype=np.float64))
+    norm = ctypes.c_double()
+    c = lib().oracle_clip_coefficient(_ptr(arr), arr.size, max_norm, ctypes.byref(norm))
+    return float(np.float32(c)), norm.value
+
+
+def step(reps, scale: float, master, m, v, hp_arr, param_out=None, main_grad_out=None,
+         grad_coeff: float = 1.0) -> None:
     n = master.size
     for a in (master, m, v):
         _check(a, np.float32, n)
@@ -124,4 +144,4 @@ def step(reps, scale: float, master, m, v, hp_arr, param_out=None, main_grad_out
         _check(main_grad_out, np.float32, n)
     keep = list(reps)
     lib().oracle_step(len(keep), _rep_array(keep, n), scale, n, _ptr(master), _ptr(m), _ptr(v),
-                      _ptr(param_out), _ptr(main_grad_out), _ptr(hp_arr))
+                      _ptr(param_out), _ptr(main_grad_out), _ptr(hp_arr), grad_coeff)

@@ -28,6 +28,15 @@
  *   p' = p - lr*(u + wd*p)
  * with 1-b1 and 1-b2 formed in fp32 and bc_i = 1 - b_i^t formed in double
  * by t repeated products and rounded once to fp32.
+ *
+ * Global-norm clipping (the distributed-training notes, §8.3: the squared
+ * sums of every rank's gradient shard are summed across ranks, the square
+ * root is the global norm, and clipping happens before the update).
+ * Reading: the norm is over the reduced bf16 gradient g of the owned
+ * parameter elements, squares summed in fp64; the clipping coefficient is
+ * min(1, max_norm / (norm + 1e-6)) in fp64, rounded to fp32 (the convention
+ * of PyTorch's clip_grad_norm_), and multiplies the fp32 main grad before
+ * Adam; a norm that is not finite means a skipped step (found-inf).
  */
 #include <math.h>
 #include <stdint.h>
@@ -172,17 +181,46 @@ void oracle_adam(int64_t n, const uint16_t *grad, float *master, float *m, float
     }
 }
 
+/* Sum over i of g_i^2 in double, i = 0..n-1 in order, where g is the reduced
+ * gradient of reduce_one. Sequential, so the order is the element order. */
+double oracle_norm_sq(int32_t n_rep, const uint16_t *const *rep, float scale, int64_t n)
+{
+    double total = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double g = (double)widen(reduce_one(n_rep, rep, i, scale));
+        total = total + g * g;
+    }
+    return total;
+}
+
+/* Clipping coefficient from the ranks' squared norms, summed in index order.
+ * A NaN result means: skip the step (the norm is not finite). */
+float oracle_clip_coefficient(const double *parts, int32_t n, float max_norm, double *norm_out)
+{
+    double total = 0.0;
+    for (int32_t i = 0; i < n; ++i)
+        total = total + parts[i];
+    double norm = sqrt(total);
+    if (norm_out)
+        *norm_out = norm;
+    if (!isfinite(norm))
+        return NAN;
+    double c = (double)max_norm / (norm + 1e-6);
+    return (float)(c < 1.0 ? c : 1.0);
+}
+
 /* The whole step for n contiguous owned elements: reduce the n_rep
- * contributions, copy into the fp32 main grad (also stored to main_grad_out
- * when not NULL), Adam, bf16 write-back to param_out when not NULL. */
+ * contributions, copy into the fp32 main grad and multiply it by grad_coeff
+ * (1 without clipping; the product is also stored to main_grad_out when not
+ * NULL), Adam, bf16 write-back to param_out when not NULL. */
 void oracle_step(int32_t n_rep, const uint16_t *const *rep, float scale, int64_t n,
                  float *master, float *m, float *v, uint16_t *param_out,
-                 float *main_grad_out, const float *hp_in)
+                 float *main_grad_out, const float *hp_in, float grad_coeff)
 {
     oracle_hp hp = {hp_in[0], hp_in[1], hp_in[2], hp_in[3], hp_in[4], hp_in[5], hp_in[6]};
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
-        float g = widen(reduce_one(n_rep, rep, i, scale));
+        float g = widen(reduce_one(n_rep, rep, i, scale)) * grad_coeff;
         if (main_grad_out)
             main_grad_out[i] = g;
         adam_one(&hp, g, &master[i], &m[i], &v[i]);

@@ -34,8 +34,12 @@ def _span(coords, world: L.Range, local_start: int):
 def rank_step(layout: L.Layout, rank: int, grads, grad_coords: int, scale: float,
               master: np.ndarray, m: np.ndarray, v: np.ndarray, hp_arr: np.ndarray,
               param_out: np.ndarray | None = None, param_coords: int = WORLD,
-              main_grad_out: np.ndarray | None = None) -> None:
-    """Rank `rank`'s step, in place on master/m/v ([L] fp32) and param_out."""
+              main_grad_out: np.ndarray | None = None, grad_coeff: float = 1.0) -> None:
+    """Rank `rank`'s step, in place on master/m/v ([L] fp32) and param_out.
+    grad_coeff multiplies the fp32 main grad (global-norm clipping); a NaN
+    coefficient means a skipped step: nothing changes."""
+    if np.isnan(grad_coeff):
+        return
     for pc in L.rank_pieces(layout, rank):
         k0 = pc.shard_offset
         k1 = k0 + pc.gbuf_world.size
@@ -46,7 +50,18 @@ def rank_step(layout: L.Layout, rank: int, grads, grad_coords: int, scale: float
             p0, p1 = _span(param_coords, pc.gbuf_world, k0)
             po = param_out[p0:p1]
         mg = None if main_grad_out is None else main_grad_out[k0:k1]
-        N.step(reps, scale, master[k0:k1], m[k0:k1], v[k0:k1], hp_arr, po, mg)
+        N.step(reps, scale, master[k0:k1], m[k0:k1], v[k0:k1], hp_arr, po, mg, grad_coeff)
+
+
+def rank_norm_sq(layout: L.Layout, rank: int, grads, grad_coords: int, scale: float) -> float:
+    """The rank's squared gradient norm: squares of the reduced gradient over
+    its owned elements, summed in fp64 in shard order (pieces in order, the
+    elements of each in order)."""
+    total = 0.0
+    for pc in L.rank_pieces(layout, rank):
+        g0, g1 = _span(grad_coords, pc.gbuf_world, pc.shard_offset)
+        total = total + N.norm_sq([g[g0:g1] for g in grads], scale)
+    return total
 
 
 def reduce_scatter(layout: L.Layout, rank: int, grads, grad_coords: int, scale: float,

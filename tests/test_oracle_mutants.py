@@ -43,6 +43,10 @@ def _numeric_pins():
         TN.test_adam_special_cases,
         TN.test_adam_matches_torch_adamw,
         TN.test_step_is_reduce_then_adam,
+        TN.test_norm_sq_exact_on_integers,
+        TN.test_clip_coefficient_matches_torch,
+        TN.test_clip_coefficient_special_cases,
+        TN.test_clipped_step,
     ]
 
 
@@ -95,9 +99,20 @@ C_MUTANTS = {
          "float acc = widen(narrow(widen(rep[n_rep - 1][i]) * scale));\n    for (int32_t j = 1; j < n_rep; ++j) {\n"
          "        float term = widen(narrow(widen(rep[n_rep - 1 - j][i]) * scale));"),
     ],
-    "no rounding of the reduced sum": [("    return narrow(acc);\n}", "    return narrow(acc) | 0;\n}"),
-                                       ("float g = widen(reduce_one(n_rep, rep, i, scale));",
-                                        "float g = widen(reduce_one(n_rep, rep, i, scale)) * 1.0000001f;")],
+    "reduced sum truncated instead of rounded": [
+        ("    return narrow(acc);\n}",
+         "    uint32_t bits;\n    memcpy(&bits, &acc, sizeof bits);\n    return (uint16_t)(bits >> 16);\n}")],
+    "norm squares of rank 0's contribution only": [
+        ("double g = (double)widen(reduce_one(n_rep, rep, i, scale));", "double g = (double)widen(rep[0][i]);")],
+    "norm squares without the scaling": [
+        ("double g = (double)widen(reduce_one(n_rep, rep, i, scale));",
+         "double g = (double)widen(reduce_one(n_rep, rep, i, 1.0f));")],
+    "clip coefficient from the squared norm": [("double norm = sqrt(total);", "double norm = total;")],
+    "clip coefficient not capped at 1": [("return (float)(c < 1.0 ? c : 1.0);", "return (float)c;")],
+    "found-inf not detected": [("    if (!isfinite(norm))\n        return NAN;\n", "")],
+    "clipping coefficient ignored": [
+        ("float g = widen(reduce_one(n_rep, rep, i, scale)) * grad_coeff;",
+         "float g = widen(reduce_one(n_rep, rep, i, scale));")],
     "weight decay with the wrong sign": [("float u2 = u + wdp;", "float u2 = u - wdp;")],
     "weight decay not scaled by lr": [("float st = hp->lr * u2;", "float st = hp->lr * u + wdp;")],
     "weight decay dropped": [("float u2 = u + wdp;", "float u2 = u;")],

@@ -4,7 +4,9 @@
     training notes (section "AllReduce") and against exact rational sums;
   * scaling before the reduction (page "04 · 分布式优化器", §5) as an
     observable order;
-  * Adam against closed forms at step 1 and against torch.optim.AdamW.
+  * Adam against closed forms at step 1 and against torch.optim.AdamW;
+  * the global-norm clipping of the distributed-training notes (§8.3) against
+    exact integer sums and torch.nn.utils.clip_grad_norm_.
 """
 
 import math
@@ -344,3 +346,97 @@ def test_step_is_reduce_then_adam():
     assert np.array_equal(pa, pb)
     assert np.array_equal(mga, N.widen(red))
     assert np.array_equal(pa, torch_bf16_bits(a[0]))
+
+
+# ---- global-norm clipping ----------------------------------------------------------------
+
+def test_norm_sq_exact_on_integers():
+    # squares of integers below 2^8, summed: exact in fp64, so any order agrees
+    rng = np.random.default_rng(31)
+    D, n = 4, 20_000
+    ints = [rng.integers(-60, 60, size=n) for _ in range(D)]
+    reps = [torch_bf16_bits(x.astype(np.float32)) for x in ints]
+    total = np.sum(np.stack(ints), axis=0)                # |sum| < 240: exact in bf16
+    want = float(np.sum(total.astype(np.int64) ** 2))
+    assert N.norm_sq(reps, 1.0) == want
+    # the scale applies to each term before the sum (page 1, §5): scale 1/2 -> (sum/2)^2
+    assert N.norm_sq(reps, 0.5) == float(np.sum((total.astype(np.float64) / 2) ** 2))
+
+
+def test_clip_coefficient_matches_torch():
+    """The coefficient, applied to a gradient, gives torch.nn.utils.clip_grad_norm_'s
+    clipped gradient (fp32) to within a few ulp."""
+    rng = np.random.default_rng(32)
+    for max_norm in (0.05, 0.5, 1.0, 10.0, 1e4):
+        shards = [(rng.standard_normal(4000) * 1e-2).astype(np.float32) for _ in range(4)]
+        parts = [float(np.sum(x.astype(np.float64) ** 2)) for x in shards]
+        coeff, norm = N.clip_coefficient(parts, max_norm)
+        assert abs(norm - np.sqrt(sum(parts))) <= 1e-12 * norm
+        ps = [torch.nn.Parameter(torch.zeros(4000)) for _ in range(4)]
+        for p, x in zip(ps, shards):
+            p.grad = torch.from_numpy(x.copy())
+        total = torch.nn.utils.clip_grad_norm_(ps, max_norm, norm_type=2.0, foreach=False)
+        assert abs(float(total) - norm) <= 1e-6 * norm
+        for p, x in zip(ps, shards):
+            mine = x * np.float32(coeff)
+            np.testing.assert_allclose(mine, p.grad.numpy(), rtol=4e-7, atol=1e-12)
+
+
+def test_clip_coefficient_special_cases():
+    # below the threshold nothing is clipped
+    assert N.clip_coefficient([0.25, 0.0], 1.0)[0] == 1.0
+    assert N.clip_coefficient([0.0], 1.0)[0] == 1.0
+    # above it the clipped norm is max_norm: coefficient * norm == max_norm (up to the 1e-6)
+    c, norm = N.clip_coefficient([16.0, 9.0], 1.0)
+    assert norm == 5.0 and abs(c * 5.0 - 1.0) < 1e-6
+    # a norm that is not finite is found-inf: NaN coefficient, the step is skipped
+    assert np.isnan(N.clip_coefficient([1.0, np.inf], 1.0)[0])
+    assert np.isnan(N.clip_coefficient([np.nan, 1.0], 1.0)[0])
+    # parts are summed in index order
+    big, tiny = 2.0**60, 1.0
+    assert N.clip_coefficient([big, tiny, -big], 1.0)[1] == 0.0
+    assert N.clip_coefficient([big, -big, tiny], 1.0)[1] == 1.0
+
+
+def test_clipped_step():
+    rng = np.random.default_rng(33)
+    D, n = 4, 10_000
+    reps = [torch_bf16_bits((rng.standard_normal(n) * 1e-2).astype(np.float32)) for _ in range(D)]
+    p0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m0 = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    v0 = ((rng.standard_normal(n) * 1e-3) ** 2).astype(np.float32)
+    hp = N.hp_array(HP, 5)
+    # coefficient 1 is the unclipped step, bit for bit
+    a = [p0.copy(), m0.copy(), v0.copy()]
+    b = [p0.copy(), m0.copy(), v0.copy()]
+    N.step(reps, 0.25, *a, hp)
+    N.step(reps, 0.25, *b, hp, grad_coeff=1.0)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    # a coefficient c is Adam on the main grad multiplied by c (one fp32 product)
+    c = float(np.float32(0.3721))
+    mg = np.zeros(n, np.float32)
+    st = [p0.copy(), m0.copy(), v0.copy()]
+    N.step(reps, 0.25, *st, hp, main_grad_out=mg, grad_coeff=c)
+    red = N.reduce(reps, 0.25)
+    assert np.array_equal(mg, N.widen(red) * np.float32(c))
+    ref = [p0.copy(), m0.copy(), v0.copy()]
+    N.adam(red, *ref, hp)
+    assert not np.array_equal(ref[1], st[1])
+    # closed form at step 1 from zero state: the moments see the clipped grad g'
+    z = [p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)]
+    g1 = np.zeros(n, np.float32)
+    N.step(reps, 0.25, *z, N.hp_array(HP, 1), main_grad_out=g1, grad_coeff=c)
+    b1, b2 = np.float32(HP["beta1"]), np.float32(HP["beta2"])
+    assert np.array_equal(z[1], (np.float32(1) - b1) * g1)
+    assert np.array_equal(z[2], (np.float32(1) - b2) * (g1 * g1))
+    # a NaN coefficient (found-inf) through the rank composition changes nothing
+    lay = L.build_layout([3000, 7000], 4000, D)
+    st2 = [S.gather_shard(lay, 1, x) for x in (np.resize(p0, lay.buffer_numel),) * 3]
+    before = [x.copy() for x in st2]
+    par = np.full(lay.buffer_numel, 0x7FBF, np.uint16)
+    full = [np.resize(r, lay.buffer_numel) for r in reps]
+    S.rank_step(lay, 1, full, S.WORLD, 0.25, *st2, hp, par, S.WORLD, grad_coeff=float("nan"))
+    for x, y in zip(st2, before):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    assert (par == 0x7FBF).all()

@@ -19,9 +19,10 @@
  *
  * Conventions for every call:
  *   - bf16 values are passed as uint16_t bit patterns.
- *   - Device pointers are caller-owned, must be 16-byte aligned, and point
- *     to memory of the device the plan was built on. Host arrays (the
- *     replica pointer list, param_numel, hp) are read during the call only.
+ *   - Device pointers are caller-owned, must be 16-byte aligned (device
+ *     scalars: naturally aligned), and point to memory of the device the
+ *     plan was built on. Host arrays (the replica pointer list, param_numel,
+ *     hp) are read during the call only.
  *   - `stream` is a hipStream_t (NULL = the default stream). Calls that take
  *     one only enqueue work on it and return; they never allocate device
  *     memory and never synchronise the host.
@@ -55,7 +56,7 @@ extern "C" {
 
 #define ZDO_OK 0
 #define ZDO_EINVAL (-1)   /* bad argument (size, rank, coords, count, NULL) */
-#define ZDO_EALIGN (-2)   /* a device pointer is not 16-byte aligned */
+#define ZDO_EALIGN (-2)   /* a device pointer is not aligned as required */
 #define ZDO_EALIAS (-3)   /* outputs overlap each other or the inputs illegally */
 #define ZDO_EHIP (-4)     /* HIP runtime or launch failure; no device for the plan */
 #define ZDO_ENOMEM (-5)   /* host or device allocation failed */
@@ -179,6 +180,63 @@ int sharded_adam_step(const zdo_plan *plan, const uint16_t *const *grads, int32_
  * elements; must not overlap. */
 int writeback_params(const zdo_plan *plan, const float *master, uint16_t *param_out,
                      int32_t param_coords, void *stream);
+
+/* ---- global-norm clipping ---------------------------------------------------
+ * The distributed-training notes, §8.3: each rank's squared gradient sum is
+ * all-reduced into the global norm sqrt(sum_i ||g_i||^2), and the gradients
+ * are clipped before the optimizer update. Here: g is the rank's reduced
+ * bf16 gradient over its owned parameter elements (as sharded_adam_step
+ * computes it); grad_norm_sq gives the rank's share, the caller sums the
+ * ranks' shares (a collective across GPUs; a device array here) with
+ * clip_coefficient, and sharded_adam_step_clipped applies the coefficient.
+ * Nothing here synchronises the host: the coefficient stays in device memory.
+ */
+
+/* Workspace bytes grad_norm_sq needs for this plan: 8 per 512-element tile of
+ * the rank's owned elements, at least 8. */
+int64_t zdo_plan_norm_workspace_bytes(const zdo_plan *plan);
+
+/* The rank's squared gradient norm: sum over its owned parameter elements of
+ * g^2, g = bf16(sum_j bf16(scale * g_j)) exactly as in sharded_adam_step,
+ * squares (exact in fp64) summed in fp64 in a fixed order: per 512-element
+ * tile (lanes' 8 elements in order, then a fixed butterfly over the 64
+ * lanes) into `workspace`, then the tiles by a fixed tree into
+ * *norm_sq_out. Run to run the result is bit-identical; against a
+ * sequential fp64 sum it differs only by fp64 rounding.
+ * replicas / n_replicas / replica_coords: as sharded_adam_step's grads
+ * (n_replicas = D, or 1 for an already reduced buffer with scale 1).
+ * reduced_out: NULL, or bf16 N (out_coords ZDO_WORLD) / L (ZDO_LOCAL)
+ * elements receiving g at the owned elements only (then sharded_adam_step
+ * with n_grads = 1 and scale 1 on it reads 2 bytes per element instead of
+ * 2D); it may coincide exactly with a replica in the same coordinates.
+ * workspace: device, zdo_plan_norm_workspace_bytes(plan) bytes, 16-byte
+ * aligned, used by this call only until it completes on `stream` (calls that
+ * overlap in time need separate workspaces). norm_sq_out: device double,
+ * 8-byte aligned. A rank that owns nothing gets 0. */
+int grad_norm_sq(const zdo_plan *plan, const uint16_t *const *replicas, int32_t n_replicas,
+                 int32_t replica_coords, float scale, uint16_t *reduced_out, int32_t out_coords,
+                 void *workspace, double *norm_sq_out, void *stream);
+
+/* From n_parts squared norms (device doubles, e.g. every rank's grad_norm_sq),
+ * summed in index order in fp64: norm = sqrt(total) and the clipping
+ * coefficient min(1, max_norm / (norm + 1e-6)) computed in fp64 and rounded to
+ * fp32, written to *coeff_out (device float, 4-byte aligned); NaN if the norm
+ * is not finite (found-inf: sharded_adam_step_clipped then skips the step).
+ * norm_out: NULL or a device double receiving the norm. One work-item. */
+int clip_coefficient(const double *norm_sq_parts, int32_t n_parts, float max_norm, float *coeff_out,
+                     double *norm_out, void *stream);
+
+/* sharded_adam_step with global-norm clipping: the fp32 main grad is
+ * multiplied by *grad_coeff (a device float read by the kernel, e.g. from
+ * clip_coefficient) before Adam, and main_grad_out receives the product. If
+ * *grad_coeff is NaN the call changes nothing (found-inf skip). With
+ * *grad_coeff == 1 the results equal sharded_adam_step's bit for bit. All
+ * other arguments and rules as sharded_adam_step. */
+int sharded_adam_step_clipped(const zdo_plan *plan, const uint16_t *const *grads, int32_t n_grads,
+                              int32_t grad_coords, float scale, float *master, float *exp_avg,
+                              float *exp_avg_sq, uint16_t *param_out, int32_t param_coords,
+                              const zdo_adam *hp, const float *grad_coeff, float *main_grad_out,
+                              void *stream);
 
 /* ---- measurement helper (not part of the method) -------------------------- */
 

@@ -27,7 +27,7 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     L = Z.require_library()
     names = header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 19, names
     assert sorted(Z.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -122,7 +122,15 @@ def test_launch_on_host_only_plan_is_an_error():
     assert L.sharded_adam_step(plan.handle, reps, 2, 0, 1.0, 64, 80, 96, None, 0, ctypes.byref(hp), None,
                                None) == Z.EHIP
     assert L.writeback_params(plan.handle, 64, 48, 0, None) == Z.EHIP
+    assert L.grad_norm_sq(plan.handle, reps, 2, 0, 1.0, None, 0, 64, 128, None) == Z.EHIP
+    assert L.sharded_adam_step_clipped(plan.handle, reps, 2, 0, 1.0, 64, 80, 96, None, 0, ctypes.byref(hp), 112,
+                                       None, None) == Z.EHIP
     assert b"device" in L.zdo_last_error()
+    assert L.zdo_plan_norm_workspace_bytes(plan.handle) >= 8
+    assert L.clip_coefficient(None, 1, 1.0, 64, None, None) == Z.EINVAL
+    assert L.clip_coefficient(64, 0, 1.0, 128, None, None) == Z.EINVAL
+    assert L.clip_coefficient(68, 1, 1.0, 128, None, None) == Z.EALIGN
+    assert L.clip_coefficient(64, 2, 1.0, 72, None, None) == Z.EALIAS
     assert L.zdo_device_copy(16, 48, 15, None) == Z.EINVAL
     assert L.zdo_device_copy(16, 40, 16, None) == Z.EALIGN
     assert L.zdo_device_copy(16, 32, 32, None) == Z.EALIAS

@@ -66,7 +66,8 @@ BUCKET_DTYPE = np.dtype([("offset", "<i8"), ("numel", "<i8"), ("padded_numel", "
 EXPORTS = ("build_range_map", "zdo_plan_destroy", "zdo_plan_buffer_numel", "zdo_plan_shard_numel",
            "zdo_plan_owned_numel", "zdo_plan_dp_size", "zdo_plan_rank", "zdo_plan_buckets",
            "zdo_plan_pieces", "reduce_scatter_local", "force_all_reduce", "sharded_adam_step",
-           "writeback_params", "zdo_device_copy", "zdo_last_error")
+           "writeback_params", "zdo_plan_norm_workspace_bytes", "grad_norm_sq", "clip_coefficient",
+           "sharded_adam_step_clipped", "zdo_device_copy", "zdo_last_error")
 
 _lib = None
 
@@ -96,11 +97,18 @@ def require_library() -> ctypes.CDLL:
     L.force_all_reduce.argtypes = [vp, vp, i32, f32, vp, vp]
     L.sharded_adam_step.argtypes = [vp, vp, i32, i32, f32, vp, vp, vp, vp, i32, ctypes.POINTER(Adam), vp, vp]
     L.writeback_params.argtypes = [vp, vp, vp, i32, vp]
+    L.zdo_plan_norm_workspace_bytes.argtypes = [vp]
+    L.zdo_plan_norm_workspace_bytes.restype = i64
+    L.grad_norm_sq.argtypes = [vp, vp, i32, i32, f32, vp, i32, vp, vp, vp]
+    L.clip_coefficient.argtypes = [vp, i32, f32, vp, vp, vp]
+    L.sharded_adam_step_clipped.argtypes = [vp, vp, i32, i32, f32, vp, vp, vp, vp, i32, ctypes.POINTER(Adam),
+                                            vp, vp, vp]
     L.zdo_device_copy.argtypes = [vp, vp, i64, vp]
     L.zdo_last_error.argtypes = []
     L.zdo_last_error.restype = ctypes.c_char_p
     for f in ("build_range_map", "zdo_plan_buckets", "zdo_plan_pieces", "reduce_scatter_local",
-              "force_all_reduce", "sharded_adam_step", "writeback_params", "zdo_device_copy"):
+              "force_all_reduce", "sharded_adam_step", "writeback_params", "grad_norm_sq", "clip_coefficient",
+              "sharded_adam_step_clipped", "zdo_device_copy"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -149,6 +157,10 @@ class Plan:
         _check(L.zdo_plan_pieces(self.handle, out.ctypes.data, n.value, ctypes.byref(n)))
         return out
 
+    @property
+    def norm_workspace_bytes(self) -> int:
+        return int(require_library().zdo_plan_norm_workspace_bytes(self.handle))
+
     def extent(self, coords: int) -> int:
         return self.buffer_numel if coords == WORLD else self.shard_numel
 
@@ -181,7 +193,8 @@ def _dev_ptr(t, what: str, kind: str, numel: int | None) -> int:
         raise TypeError(f"{what}: expected a torch tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{what}: must be a device (cuda) tensor")
-    ok = {"bf16": (torch.bfloat16, torch.int16, torch.uint16), "f32": (torch.float32,)}[kind]
+    ok = {"bf16": (torch.bfloat16, torch.int16, torch.uint16), "f32": (torch.float32,),
+          "f64": (torch.float64,), "bytes": (torch.uint8, torch.int8)}[kind]
     if t.dtype not in ok:
         raise TypeError(f"{what}: dtype {t.dtype} is not {kind}")
     if not t.is_contiguous():
@@ -238,6 +251,48 @@ def sharded_adam_step(plan: Plan, grads, grad_coords: int, scale: float, master,
     _check(require_library().sharded_adam_step(plan.handle, g, len(grads), grad_coords, scale, m, a, s, p,
                                                param_coords, ctypes.byref(hp), mg,
                                                _stream(stream, master.device)))
+
+
+def sharded_adam_step_clipped(plan: Plan, grads, grad_coords: int, scale: float, master, exp_avg, exp_avg_sq,
+                              param_out=None, param_coords: int = WORLD, *, grad_coeff, lr: float, beta1: float,
+                              beta2: float, eps: float, weight_decay: float, step: int, main_grad_out=None,
+                              stream=None) -> None:
+    """sharded_adam_step with the fp32 main grad multiplied by grad_coeff (a
+    one-element float32 device tensor; NaN skips the step)."""
+    L = plan.shard_numel
+    g = _ptr_list(grads, "grads", plan.extent(grad_coords))
+    m = _dev_ptr(master, "master", "f32", L)
+    a = _dev_ptr(exp_avg, "exp_avg", "f32", L)
+    s = _dev_ptr(exp_avg_sq, "exp_avg_sq", "f32", L)
+    p = None if param_out is None else _dev_ptr(param_out, "param_out", "bf16", plan.extent(param_coords))
+    mg = None if main_grad_out is None else _dev_ptr(main_grad_out, "main_grad_out", "f32", L)
+    c = _dev_ptr(grad_coeff, "grad_coeff", "f32", 1)
+    hp = adam_hparams(lr, beta1, beta2, eps, weight_decay, step)
+    _check(require_library().sharded_adam_step_clipped(plan.handle, g, len(grads), grad_coords, scale, m, a, s, p,
+                                                       param_coords, ctypes.byref(hp), c, mg,
+                                                       _stream(stream, master.device)))
+
+
+def grad_norm_sq(plan: Plan, replicas, replica_coords: int, scale: float, workspace, norm_sq_out,
+                 reduced_out=None, out_coords: int = WORLD, stream=None) -> None:
+    """The rank's squared gradient norm into norm_sq_out (one-element float64
+    device tensor); workspace: uint8 device tensor of plan.norm_workspace_bytes."""
+    reps = _ptr_list(replicas, "replicas", plan.extent(replica_coords))
+    ws = _dev_ptr(workspace, "workspace", "bytes", plan.norm_workspace_bytes)
+    ns = _dev_ptr(norm_sq_out, "norm_sq_out", "f64", 1)
+    ro = None if reduced_out is None else _dev_ptr(reduced_out, "reduced_out", "bf16", plan.extent(out_coords))
+    _check(require_library().grad_norm_sq(plan.handle, reps, len(replicas), replica_coords, scale, ro, out_coords,
+                                          ws, ns, _stream(stream, norm_sq_out.device)))
+
+
+def clip_coefficient(norm_sq_parts, max_norm: float, coeff_out, norm_out=None, stream=None) -> None:
+    """Global norm from the ranks' squared norms (float64 device tensor) and the
+    clipping coefficient into coeff_out (one-element float32 device tensor)."""
+    parts = _dev_ptr(norm_sq_parts, "norm_sq_parts", "f64", 1)
+    c = _dev_ptr(coeff_out, "coeff_out", "f32", 1)
+    n = None if norm_out is None else _dev_ptr(norm_out, "norm_out", "f64", 1)
+    _check(require_library().clip_coefficient(parts, norm_sq_parts.numel(), max_norm, c, n,
+                                              _stream(stream, coeff_out.device)))
 
 
 def writeback_params(plan: Plan, master, param_out, param_coords: int, stream=None) -> None:

@@ -32,6 +32,8 @@ bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.hi 
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool aligned_to(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
 int fail(int code, const std::string &msg) {
     g_error = msg;
     return code;
@@ -250,10 +252,10 @@ int force_all_reduce(const zdo_plan *plan, const uint16_t *const *replicas, int3
     return launch_result(launch_reduce(a, plan->lds_per_cu, static_cast<hipStream_t>(stream)), fn);
 }
 
-int sharded_adam_step(const zdo_plan *plan, const uint16_t *const *grads, int32_t n_grads, int32_t grad_coords,
-                      float scale, float *master, float *exp_avg, float *exp_avg_sq, uint16_t *param_out,
-                      int32_t param_coords, const zdo_adam *hp, float *main_grad_out, void *stream) {
-    const char *fn = "sharded_adam_step";
+static int adam_step(const char *fn, const zdo_plan *plan, const uint16_t *const *grads, int32_t n_grads,
+                     int32_t grad_coords, float scale, float *master, float *exp_avg, float *exp_avg_sq,
+                     uint16_t *param_out, int32_t param_coords, const zdo_adam *hp, const float *coeff,
+                     float *main_grad_out, void *stream) {
     if (int rc = check_plan(plan, fn))
         return rc;
     if (n_grads != plan->dp_size && n_grads != 1)
@@ -286,6 +288,8 @@ int sharded_adam_step(const zdo_plan *plan, const uint16_t *const *grads, int32_
     if (main_grad_out)
         if (int rc = check_ptr(main_grad_out, fn, "main_grad_out"))
             return rc;
+    if (coeff && !aligned_to(coeff, 4))
+        return fail(ZDO_EALIGN, std::string(fn) + ": grad_coeff is not 4-byte aligned");
     const int64_t L = plan->shard_numel;
     // Every written buffer must be disjoint from every other buffer.
     struct Named {
@@ -309,6 +313,8 @@ int sharded_adam_step(const zdo_plan *plan, const uint16_t *const *grads, int32_
             if (overlap(written[i].s, gs[j]))
                 return fail(ZDO_EALIAS, std::string(fn) + ": " + written[i].name + " overlaps grad " +
                                             std::to_string(j));
+        if (coeff && overlap(written[i].s, span_of(coeff, 1, 4)))
+            return fail(ZDO_EALIAS, std::string(fn) + ": " + written[i].name + " overlaps grad_coeff");
     }
     a.walk = {plan->d_param_segs, plan->d_param_tile_seg, plan->param_tiles, 0, int64_t(plan->param_segs.size())};
     a.nrep = n_grads;
@@ -320,6 +326,7 @@ int sharded_adam_step(const zdo_plan *plan, const uint16_t *const *grads, int32_
     a.v = exp_avg_sq;
     a.param = param_out;
     a.main_grad = main_grad_out;
+    a.coeff = coeff;
     a.c.lr = hp->lr;
     a.c.b1 = hp->beta1;
     a.c.b2 = hp->beta2;
@@ -330,6 +337,100 @@ int sharded_adam_step(const zdo_plan *plan, const uint16_t *const *grads, int32_
     a.c.bc1 = bias_correction(hp->beta1, hp->step);
     a.c.bc2 = bias_correction(hp->beta2, hp->step);
     return launch_result(launch_step(a, plan->lds_per_cu, static_cast<hipStream_t>(stream)), fn);
+}
+
+int sharded_adam_step(const zdo_plan *plan, const uint16_t *const *grads, int32_t n_grads, int32_t grad_coords,
+                      float scale, float *master, float *exp_avg, float *exp_avg_sq, uint16_t *param_out,
+                      int32_t param_coords, const zdo_adam *hp, float *main_grad_out, void *stream) {
+    return adam_step("sharded_adam_step", plan, grads, n_grads, grad_coords, scale, master, exp_avg, exp_avg_sq,
+                     param_out, param_coords, hp, nullptr, main_grad_out, stream);
+}
+
+int sharded_adam_step_clipped(const zdo_plan *plan, const uint16_t *const *grads, int32_t n_grads,
+                              int32_t grad_coords, float scale, float *master, float *exp_avg, float *exp_avg_sq,
+                              uint16_t *param_out, int32_t param_coords, const zdo_adam *hp,
+                              const float *grad_coeff, float *main_grad_out, void *stream) {
+    if (!grad_coeff)
+        return fail(ZDO_EINVAL, "sharded_adam_step_clipped: grad_coeff is NULL");
+    return adam_step("sharded_adam_step_clipped", plan, grads, n_grads, grad_coords, scale, master, exp_avg,
+                     exp_avg_sq, param_out, param_coords, hp, grad_coeff, main_grad_out, stream);
+}
+
+int64_t zdo_plan_norm_workspace_bytes(const zdo_plan *p) {
+    if (!p)
+        return -1;
+    return p->param_tiles > 0 ? p->param_tiles * int64_t(sizeof(double)) : int64_t(sizeof(double));
+}
+
+int grad_norm_sq(const zdo_plan *plan, const uint16_t *const *replicas, int32_t n_replicas, int32_t replica_coords,
+                 float scale, uint16_t *reduced_out, int32_t out_coords, void *workspace, double *norm_sq_out,
+                 void *stream) {
+    const char *fn = "grad_norm_sq";
+    if (int rc = check_plan(plan, fn))
+        return rc;
+    if (n_replicas != plan->dp_size && n_replicas != 1)
+        return fail(ZDO_EINVAL, std::string(fn) + ": n_replicas must be the DP size " +
+                                    std::to_string(plan->dp_size) + " or 1 (pre-reduced)");
+    if (int rc = check_coords(replica_coords, fn, "replica_coords"))
+        return rc;
+    if (reduced_out)
+        if (int rc = check_coords(out_coords, fn, "out_coords"))
+            return rc;
+    NormArgs a{};
+    Span spans[ZDO_MAX_REPLICAS];
+    if (int rc = take_replicas(plan, replicas, n_replicas, replica_coords, fn, a.rep, spans))
+        return rc;
+    if (reduced_out)
+        if (int rc = check_ptr(reduced_out, fn, "reduced_out"))
+            return rc;
+    if (int rc = check_ptr(workspace, fn, "workspace"))
+        return rc;
+    if (!norm_sq_out)
+        return fail(ZDO_EINVAL, std::string(fn) + ": norm_sq_out is NULL");
+    if (!aligned_to(norm_sq_out, 8))
+        return fail(ZDO_EALIGN, std::string(fn) + ": norm_sq_out is not 8-byte aligned");
+    const Span ws = span_of(workspace, zdo_plan_norm_workspace_bytes(plan), 1);
+    const Span ns = span_of(norm_sq_out, 1, 8);
+    if (overlap(ws, ns))
+        return fail(ZDO_EALIAS, std::string(fn) + ": workspace overlaps norm_sq_out");
+    for (int32_t j = 0; j < n_replicas; ++j)
+        if (overlap(ws, spans[j]) || overlap(ns, spans[j]))
+            return fail(ZDO_EALIAS, std::string(fn) + ": workspace or norm_sq_out overlaps replica " +
+                                        std::to_string(j));
+    if (reduced_out) {
+        const Span so = span_of(reduced_out, extent(plan, out_coords), 2);
+        if (overlap(so, ws) || overlap(so, ns))
+            return fail(ZDO_EALIAS, std::string(fn) + ": reduced_out overlaps workspace or norm_sq_out");
+        for (int32_t j = 0; j < n_replicas; ++j)
+            if (overlap(so, spans[j]) && !(reduced_out == replicas[j] && out_coords == replica_coords))
+                return fail(ZDO_EALIAS, std::string(fn) + ": reduced_out overlaps replica " + std::to_string(j) +
+                                            " without coinciding with it");
+    }
+    a.walk = {plan->d_param_segs, plan->d_param_tile_seg, plan->param_tiles, 0, int64_t(plan->param_segs.size())};
+    a.nrep = n_replicas;
+    a.in_local = replica_coords == ZDO_LOCAL;
+    a.out_local = out_coords == ZDO_LOCAL;
+    a.scale = scale;
+    a.out = reduced_out;
+    a.partial = static_cast<double *>(workspace);
+    return launch_result(launch_norm(a, norm_sq_out, plan->lds_per_cu, static_cast<hipStream_t>(stream)), fn);
+}
+
+int clip_coefficient(const double *norm_sq_parts, int32_t n_parts, float max_norm, float *coeff_out,
+                     double *norm_out, void *stream) {
+    const char *fn = "clip_coefficient";
+    if (!norm_sq_parts || n_parts < 1)
+        return fail(ZDO_EINVAL, std::string(fn) + ": need at least one squared norm");
+    if (!coeff_out)
+        return fail(ZDO_EINVAL, std::string(fn) + ": coeff_out is NULL");
+    if (!aligned_to(norm_sq_parts, 8) || !aligned_to(coeff_out, 4) || (norm_out && !aligned_to(norm_out, 8)))
+        return fail(ZDO_EALIGN, std::string(fn) + ": a pointer is not naturally aligned");
+    const Span ps = span_of(norm_sq_parts, n_parts, 8), cs = span_of(coeff_out, 1, 4);
+    if (overlap(ps, cs) || (norm_out && (overlap(ps, span_of(norm_out, 1, 8)) ||
+                                         overlap(cs, span_of(norm_out, 1, 8)))))
+        return fail(ZDO_EALIAS, std::string(fn) + ": outputs overlap each other or the squared norms");
+    return launch_result(launch_clip(norm_sq_parts, n_parts, max_norm, coeff_out, norm_out,
+                                     static_cast<hipStream_t>(stream)), fn);
 }
 
 int writeback_params(const zdo_plan *plan, const float *master, uint16_t *param_out, int32_t param_coords,

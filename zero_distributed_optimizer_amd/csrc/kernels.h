@@ -42,7 +42,19 @@ struct StepArgs {
     float *master, *m, *v;
     uint16_t *param;     // may be NULL
     float *main_grad;    // may be NULL
+    const float *coeff;  // device clipping coefficient, or NULL for none
     AdamConst c;
+};
+
+struct NormArgs {
+    Walk walk;
+    const uint16_t *rep[ZDO_MAX_REPLICAS];
+    int32_t nrep;
+    int32_t in_local;
+    int32_t out_local;
+    float scale;
+    uint16_t *out;       // reduced gradient at the owned elements, or NULL
+    double *partial;     // one per tile of walk
 };
 
 struct WritebackArgs {
@@ -58,5 +70,10 @@ hipError_t launch_reduce(const ReduceArgs &a, int lds_per_cu, hipStream_t stream
 hipError_t launch_step(const StepArgs &a, int lds_per_cu, hipStream_t stream);
 hipError_t launch_writeback(const WritebackArgs &a, int lds_per_cu, hipStream_t stream);
 hipError_t launch_copy(void *dst, const void *src, int64_t n16, hipStream_t stream);
+// Squared norm: per-tile partials into a.partial, then their fixed-order sum
+// into *norm_sq (0 when a.walk has no tiles).
+hipError_t launch_norm(const NormArgs &a, double *norm_sq, int lds_per_cu, hipStream_t stream);
+hipError_t launch_clip(const double *parts, int32_t n, float max_norm, float *coeff, double *norm_out,
+                       hipStream_t stream);
 
 }  // namespace zdo

@@ -193,6 +193,15 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceArgs a) {
 
 template <int D>
 __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a) {
+    // Global-norm clipping: the main grad is multiplied by the coefficient; a
+    // NaN coefficient (found-inf) leaves everything unchanged.
+    const bool clip = a.coeff != nullptr;
+    float cf = 1.0f;
+    if (clip) {
+        cf = *a.coeff;
+        if (cf != cf)
+            return;
+    }
     for (int64_t tile = blockIdx.x; tile < a.walk.ntiles; tile += gridDim.x) {
         ChunkPos c;
         if (!chunk_of(a.walk, tile, c))
@@ -209,6 +218,11 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a) {
                 const uint32_t r = to_bf16x2(acc[2 * k], acc[2 * k + 1]);
                 g[2 * k] = lo_f32(r);
                 g[2 * k + 1] = hi_f32(r);
+            }
+            if (clip) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    g[e] = g[e] * cf;
             }
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -243,7 +257,9 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a) {
         } else {
             for (int e = c.lo; e < c.hi; ++e) {
                 const float acc = reduce_one<D>(a.rep, a.nrep, gi + e, a.scale);
-                const float g = lo_f32(to_bf16x2(acc, 0.0f));
+                float g = lo_f32(to_bf16x2(acc, 0.0f));
+                if (clip)
+                    g = g * cf;
                 float p = a.master[k0 + e], m = a.m[k0 + e], v = a.v[k0 + e];
                 adam(a.c, g, p, m, v);
                 a.master[k0 + e] = p;
@@ -256,6 +272,90 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a) {
             }
         }
     }
+}
+
+// ---- squared gradient norm -----------------------------------------------------------------
+// Per tile: each lane sums the squares of its chunk's elements in order (each
+// square is exact in fp64: a bf16 has an 8-bit significand), then a fixed
+// butterfly over the wave's 64 lanes gives every lane the same tile total.
+static_assert(kBlock == 64, "the tile reduction below assumes one wave per workgroup");
+
+template <int D>
+__global__ __launch_bounds__(kBlock) void norm_kernel(NormArgs a) {
+    for (int64_t tile = blockIdx.x; tile < a.walk.ntiles; tile += gridDim.x) {
+        ChunkPos c;
+        double s = 0.0;
+        if (chunk_of(a.walk, tile, c)) {
+            const int64_t gi = a.in_local ? c.k0 : c.w0;
+            const int64_t oi = a.out_local ? c.k0 : c.w0;
+            if (c.lo == 0 && c.hi == kChunk) {
+                float acc[8];
+                reduce_chunk<D>(a.rep, a.nrep, gi, a.scale, acc);
+                u32x4 o;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    o[k] = to_bf16x2(acc[2 * k], acc[2 * k + 1]);
+                    const double g0 = double(lo_f32(o[k])), g1 = double(hi_f32(o[k]));
+                    s = s + g0 * g0;
+                    s = s + g1 * g1;
+                }
+                if (a.out)
+                    st16(a.out + oi, o);
+            } else {
+                for (int e = c.lo; e < c.hi; ++e) {
+                    const uint32_t r = to_bf16x2(reduce_one<D>(a.rep, a.nrep, gi + e, a.scale), 0.0f);
+                    const double g = double(lo_f32(r));
+                    s = s + g * g;
+                    if (a.out)
+                        a.out[oi + e] = uint16_t(r);
+                }
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+            s = s + __shfl_xor(s, off, 64);
+        if (threadIdx.x == 0)
+            a.partial[tile] = s;
+    }
+}
+
+// Sum of n tile partials: work-item t adds tiles t, t + 1024, ... in order,
+// then a fixed tree over the 1024 work-items.
+constexpr int kSumThreads = 1024;
+
+__global__ __launch_bounds__(kSumThreads) void tile_sum_kernel(const double *partial, int64_t n, double *out) {
+    __shared__ double sh[kSumThreads];
+    double s = 0.0;
+    for (int64_t i = threadIdx.x; i < n; i += kSumThreads)
+        s = s + partial[i];
+    sh[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = kSumThreads / 2; w > 0; w >>= 1) {
+        if (int(threadIdx.x) < w)
+            sh[threadIdx.x] = sh[threadIdx.x] + sh[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0)
+        *out = sh[0];
+}
+
+// The clipping coefficient from n squared norms, summed in index order.
+__global__ __launch_bounds__(64) void clip_kernel(const double *parts, int32_t n, float max_norm, float *coeff,
+                                                  double *norm_out) {
+    if (threadIdx.x != 0)
+        return;
+    double total = 0.0;
+    for (int32_t i = 0; i < n; ++i)
+        total = total + parts[i];
+    const double norm = __builtin_sqrt(total);
+    if (norm_out)
+        *norm_out = norm;
+    if (!__builtin_isfinite(norm)) {
+        *coeff = __builtin_nanf("");
+        return;
+    }
+    const double q = double(max_norm) / (norm + 1e-6);
+    *coeff = float(q < 1.0 ? q : 1.0);
 }
 
 __global__ __launch_bounds__(kBlock) void writeback_kernel(WritebackArgs a) {
@@ -348,6 +448,33 @@ hipError_t launch_writeback(const WritebackArgs &a, int lds_per_cu, hipStream_t 
         return hipSuccess;
     hipLaunchKernelGGL(writeback_kernel, dim3(grid_for(a.walk.ntiles)), dim3(kBlock), lds_reserve(lds_per_cu), stream,
                        a);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm(const NormArgs &a, double *norm_sq, int lds_per_cu, hipStream_t stream) {
+    if (a.walk.ntiles > 0) {
+        const dim3 grid(grid_for(a.walk.ntiles)), block(kBlock);
+        const unsigned lds = lds_reserve(lds_per_cu);
+        switch (a.nrep) {
+        case 1: hipLaunchKernelGGL(norm_kernel<1>, grid, block, lds, stream, a); break;
+        case 2: hipLaunchKernelGGL(norm_kernel<2>, grid, block, lds, stream, a); break;
+        case 4: hipLaunchKernelGGL(norm_kernel<4>, grid, block, lds, stream, a); break;
+        case 8: hipLaunchKernelGGL(norm_kernel<8>, grid, block, lds, stream, a); break;
+        case 16: hipLaunchKernelGGL(norm_kernel<16>, grid, block, lds, stream, a); break;
+        case 32: hipLaunchKernelGGL(norm_kernel<32>, grid, block, lds, stream, a); break;
+        default: hipLaunchKernelGGL(norm_kernel<0>, grid, block, lds, stream, a); break;
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL(tile_sum_kernel, dim3(1), dim3(kSumThreads), 0, stream, a.partial, a.walk.ntiles, norm_sq);
+    return hipGetLastError();
+}
+
+hipError_t launch_clip(const double *parts, int32_t n, float max_norm, float *coeff, double *norm_out,
+                       hipStream_t stream) {
+    hipLaunchKernelGGL(clip_kernel, dim3(1), dim3(64), 0, stream, parts, n, max_norm, coeff, norm_out);
     return hipGetLastError();
 }
 

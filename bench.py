@@ -276,6 +276,36 @@ def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> d
                                    "achieved_gbps": gbps, "frac": gbps / PEAK_HBM_GBPS}
     log(f"reduce_scatter_local: {t * 1e6:.1f} us, {gbps:.0f} GB/s algorithmic")
     del red
+    # global-norm clipping: the rank's squared norm (writing the reduced
+    # gradient), the coefficient, the clipped step from the reduced gradient
+    E = plan.owned_numel
+    dev = reps[0].device
+    ws = torch.empty(plan.norm_workspace_bytes, dtype=torch.uint8, device=dev)
+    parts = torch.zeros(D, dtype=torch.float64, device=dev)
+    coeff = torch.empty(1, dtype=torch.float32, device=dev)
+    red = torch.empty(plan.shard_numel, dtype=torch.int16, device=dev)
+    st = [torch.zeros(plan.shard_numel, dtype=torch.float32, device=dev) for _ in range(3)]
+    par = torch.empty(plan.extent(coords), dtype=torch.int16, device=dev)
+    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, step=1)
+    r = plan.rank
+    t_norm = timed(lambda: zdo.grad_norm_sq(plan, reps, coords, w.scale, ws, parts[r:r + 1], red, zdo.LOCAL,
+                                            stream=stream))
+    t_clip = timed(lambda: zdo.clip_coefficient(parts, 1.0, coeff, stream=stream))
+    t_step = timed(lambda: zdo.sharded_adam_step_clipped(plan, [red], zdo.LOCAL, 1.0, *st, par, coords,
+                                                         grad_coeff=coeff, stream=stream, **hp))
+    t_all = t_norm + t_clip + t_step
+    out["clipped_step"] = {
+        "path": "grad_norm_sq (writes the reduced gradient) + clip_coefficient + sharded_adam_step_clipped "
+                "(n_grads = 1)",
+        "bytes_per_element": 2 * D + 30, "elements": E,
+        "norm_us": t_norm * 1e6, "clip_us": t_clip * 1e6, "step_us": t_step * 1e6, "total_us": t_all * 1e6,
+        "norm_gbps": E * (2 * D + 2) / t_norm / 1e9, "step_gbps": E * 28 / t_step / 1e9,
+        "achieved_gbps": E * (2 * D + 30) / t_all / 1e9, "frac": E * (2 * D + 30) / t_all / 1e9 / PEAK_HBM_GBPS,
+        "elements_per_s": E / t_all}
+    log(f"clipped step: norm {t_norm * 1e6:.1f} us + clip {t_clip * 1e6:.1f} us + step {t_step * 1e6:.1f} us, "
+        f"{out['clipped_step']['achieved_gbps']:.0f} GB/s algorithmic")
+    del ws, red, st, par
+
     if coords == zdo.WORLD:
         N = plan.buffer_numel
         full = torch.empty(N, dtype=torch.int16, device=reps[0].device)

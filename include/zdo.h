@@ -193,16 +193,17 @@ int writeback_params(const zdo_plan *plan, const float *master, uint16_t *param_
  */
 
 /* Workspace bytes grad_norm_sq needs for this plan: 8 per 512-element tile of
- * the rank's owned elements, at least 8. */
+ * the rank's owned elements plus 8 KiB. */
 int64_t zdo_plan_norm_workspace_bytes(const zdo_plan *plan);
 
 /* The rank's squared gradient norm: sum over its owned parameter elements of
  * g^2, g = bf16(sum_j bf16(scale * g_j)) exactly as in sharded_adam_step,
  * squares (exact in fp64) summed in fp64 in a fixed order: per 512-element
  * tile (lanes' 8 elements in order, then a fixed butterfly over the 64
- * lanes) into `workspace`, then the tiles by a fixed tree into
- * *norm_sq_out. Run to run the result is bit-identical; against a
- * sequential fp64 sum it differs only by fp64 rounding.
+ * lanes) into `workspace`, then the tile sums in two fixed levels (at most
+ * 1024 contiguous runs, then the runs) into *norm_sq_out. The order
+ * depends only on the plan, so the result is bit-identical run to run;
+ * against a sequential fp64 sum it differs only by fp64 rounding.
  * replicas / n_replicas / replica_coords: as sharded_adam_step's grads
  * (n_replicas = D, or 1 for an already reduced buffer with scale 1).
  * reduced_out: NULL, or bf16 N (out_coords ZDO_WORLD) / L (ZDO_LOCAL)

@@ -359,7 +359,8 @@ int sharded_adam_step_clipped(const zdo_plan *plan, const uint16_t *const *grads
 int64_t zdo_plan_norm_workspace_bytes(const zdo_plan *p) {
     if (!p)
         return -1;
-    return p->param_tiles > 0 ? p->param_tiles * int64_t(sizeof(double)) : int64_t(sizeof(double));
+    // one partial per tile, then up to 1024 second-level sums
+    return (p->param_tiles + 1024) * int64_t(sizeof(double));
 }
 
 int grad_norm_sq(const zdo_plan *plan, const uint16_t *const *replicas, int32_t n_replicas, int32_t replica_coords,

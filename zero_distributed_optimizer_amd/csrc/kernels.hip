@@ -319,15 +319,19 @@ __global__ __launch_bounds__(kBlock) void norm_kernel(NormArgs a) {
     }
 }
 
-// Sum of n tile partials: work-item t adds tiles t, t + 1024, ... in order,
-// then a fixed tree over the 1024 work-items.
+// Sum of n tile partials in two fixed-order levels: workgroup b of G adds
+// the contiguous run [b*chunk, min(n, (b+1)*chunk)) (work-item t takes
+// indices t, t + 1024, ... of the run in order, then a fixed tree over the
+// 1024 work-items) into level[b]; one workgroup then adds level[0..G) by the
+// same scheme into *out. The order depends on n only.
 constexpr int kSumThreads = 1024;
+constexpr int kSumGroups = 1024;
 
-__global__ __launch_bounds__(kSumThreads) void tile_sum_kernel(const double *partial, int64_t n, double *out) {
+__device__ __forceinline__ double block_sum(const double *x, int64_t n) {
     __shared__ double sh[kSumThreads];
     double s = 0.0;
     for (int64_t i = threadIdx.x; i < n; i += kSumThreads)
-        s = s + partial[i];
+        s = s + x[i];
     sh[threadIdx.x] = s;
     __syncthreads();
     for (int w = kSumThreads / 2; w > 0; w >>= 1) {
@@ -335,8 +339,22 @@ __global__ __launch_bounds__(kSumThreads) void tile_sum_kernel(const double *par
             sh[threadIdx.x] = sh[threadIdx.x] + sh[threadIdx.x + w];
         __syncthreads();
     }
+    return sh[0];
+}
+
+__global__ __launch_bounds__(kSumThreads) void tile_sum_kernel(const double *partial, int64_t n, int64_t chunk,
+                                                               double *level) {
+    const int64_t b0 = int64_t(blockIdx.x) * chunk;
+    const int64_t len = n - b0 < chunk ? n - b0 : chunk;
+    const double s = block_sum(partial + b0, len > 0 ? len : 0);
     if (threadIdx.x == 0)
-        *out = sh[0];
+        level[blockIdx.x] = s;
+}
+
+__global__ __launch_bounds__(kSumThreads) void level_sum_kernel(const double *level, int64_t g, double *out) {
+    const double s = block_sum(level, g);
+    if (threadIdx.x == 0)
+        *out = s;
 }
 
 // The clipping coefficient from n squared norms, summed in index order.
@@ -468,7 +486,17 @@ hipError_t launch_norm(const NormArgs &a, double *norm_sq, int lds_per_cu, hipSt
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL(tile_sum_kernel, dim3(1), dim3(kSumThreads), 0, stream, a.partial, a.walk.ntiles, norm_sq);
+    // level 1: G <= kSumGroups runs of `chunk` partials; level 2: one workgroup
+    const int64_t n = a.walk.ntiles;
+    int64_t g = (n + kSumThreads - 1) / kSumThreads;
+    if (g > kSumGroups)
+        g = kSumGroups;
+    if (g < 1)
+        g = 1;
+    const int64_t chunk = n > 0 ? (n + g - 1) / g : 1;
+    double *level = a.partial + (n > 0 ? n : 0);
+    hipLaunchKernelGGL(tile_sum_kernel, dim3(unsigned(g)), dim3(kSumThreads), 0, stream, a.partial, n, chunk, level);
+    hipLaunchKernelGGL(level_sum_kernel, dim3(1), dim3(kSumThreads), 0, stream, level, g, norm_sq);
     return hipGetLastError();
 }
 

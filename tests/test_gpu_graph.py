@@ -1,0 +1,77 @@
+"""The launch calls inside a HIP graph: the clipping pipeline (squared norms of
+every rank, the coefficient, every rank's clipped step) and the plain fused
+step are captured once and replayed several times, with eager work between
+replays; every replay must equal the same calls run eagerly. The calls
+allocate nothing and never synchronise the host, and no memset is recorded
+(the norm's workspace needs no clearing)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.layout as OL
+import workloads as W
+from test_gpu_parity import DEV, SENTINEL, _gen_state, _gen_world, free, hp_kwargs
+
+pytestmark = pytest.mark.gpu
+
+
+def _pipeline(gpu, w, plans, reps, states, parts, coeff, wss, reds, params, hpk, max_norm, fused, fused_params):
+    D = w.dp_size
+    gpu.sharded_adam_step(plans[1], reps, gpu.WORLD, w.scale, *fused, fused_params, gpu.WORLD, **hpk)
+    for r in range(D):
+        gpu.grad_norm_sq(plans[r], reps, gpu.WORLD, w.scale, wss[r], parts[r:r + 1], reds[r], gpu.LOCAL)
+    gpu.clip_coefficient(parts, max_norm, coeff)
+    for r in range(D):
+        gpu.sharded_adam_step_clipped(plans[r], [reds[r]], gpu.LOCAL, 1.0, *states[r], params, gpu.WORLD,
+                                      grad_coeff=coeff, **hpk)
+
+
+@pytest.mark.parametrize("max_norm", [0.01, 1e6])
+def test_graph_replays_equal_eager(gpu, max_norm):
+    w = W.get("tiny")
+    D = w.dp_size
+    lay = OL.build_layout(w.param_numel, w.bucket_numel, D)
+    N = lay.buffer_numel
+    plans = [gpu.build_range_map(w.param_numel, w.bucket_numel, D, r) for r in range(D)]
+    reps = _gen_world(w, N)
+    hpk = hp_kwargs(w.hp, 3)
+
+    def fresh():
+        return dict(states=[_gen_state(w, p.shard_numel) for p in plans],
+                    parts=torch.zeros(D, dtype=torch.float64, device=DEV),
+                    coeff=torch.zeros(1, dtype=torch.float32, device=DEV),
+                    wss=[torch.empty(p.norm_workspace_bytes, dtype=torch.uint8, device=DEV) for p in plans],
+                    reds=[torch.empty(p.shard_numel, dtype=torch.int16, device=DEV) for p in plans],
+                    params=torch.full((N,), SENTINEL, dtype=torch.int16, device=DEV),
+                    fused=_gen_state(w, plans[1].shard_numel),
+                    fused_params=torch.full((N,), SENTINEL, dtype=torch.int16, device=DEV))
+
+    eager, graphed = fresh(), fresh()
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            _pipeline(gpu, w, plans, reps, graphed["states"], graphed["parts"], graphed["coeff"], graphed["wss"],
+                      graphed["reds"], graphed["params"], hpk, max_norm, graphed["fused"], graphed["fused_params"])
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    for replay in range(4):
+        g.replay()
+        _pipeline(gpu, w, plans, reps, eager["states"], eager["parts"], eager["coeff"], eager["wss"], eager["reds"],
+                  eager["params"], hpk, max_norm, eager["fused"], eager["fused_params"])
+        torch.cuda.synchronize()
+        # eager work between replays on the same buffers' neighbours
+        scratch = torch.randn(1 << 20, device=DEV)
+        scratch.mul_(2.0)
+        for a, b in zip(graphed["states"], eager["states"]):
+            for x, y in zip(a, b):
+                assert torch.equal(x.view(torch.int32), y.view(torch.int32)), f"replay {replay}"
+        assert torch.equal(graphed["params"], eager["params"]), f"replay {replay}"
+        for x, y in zip(graphed["fused"], eager["fused"]):
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32)), f"replay {replay} fused"
+        assert torch.equal(graphed["fused_params"], eager["fused_params"]), f"replay {replay} fused"
+        assert torch.equal(graphed["parts"], eager["parts"]) and torch.equal(graphed["coeff"], eager["coeff"])
+    del g
+    free()

@@ -509,3 +509,59 @@ def test_llama_shard_sampled(gpu, name, coords):
     assert int((par == SENTINEL).sum()) == n_rep - plan.owned_numel
     del bufs, reps, st, par
     free()
+
+
+# ---- edge cases of size and arithmetic --------------------------------------------------------
+
+@pytest.mark.parametrize("D", [64, 48])
+def test_max_replicas_runtime_path(gpu, D):
+    """D = 64 (the ABI maximum) and D = 48 take the kernels' runtime-D loop."""
+    rng = np.random.default_rng(600 + D)
+    sizes, bucket = [7000, 3, 65536, 1, 2500], 20000
+    lay = OL.build_layout(sizes, bucket, D)
+    reps_h = [bf16_host(rng, lay.buffer_numel, 1e-2) for _ in range(D)]
+    hp = W.get("tiny").hp
+    for r in (0, D // 3, D - 1):
+        Ln = OL.shard_numel(lay, r)
+        st = [(rng.standard_normal(Ln) * 0.02).astype(np.float32), np.zeros(Ln, np.float32),
+              np.zeros(Ln, np.float32)]
+        run_rank_step(gpu, sizes, bucket, D, r, reps_h, st, 1.0 / D, hp, 2, gpu.WORLD, gpu.LOCAL)
+        plan = gpu.build_range_map(sizes, bucket, D, r)
+        out = torch.full((lay.buffer_numel,), SENTINEL, dtype=torch.int16, device=DEV)
+        gpu.reduce_scatter_local(plan, [to_dev(x) for x in reps_h], gpu.WORLD, 1.0 / D, out, gpu.WORLD)
+        want = np.full(lay.buffer_numel, SENTINEL, np.uint16)
+        OS.reduce_scatter(lay, r, reps_h, OS.WORLD, 1.0 / D, want, OS.WORLD)
+        assert_bf16(host_u16(out), want, f"rs D={D} r={r}")
+    free()
+
+
+@pytest.mark.parametrize("scale", [0.0, -1.0, 3.0e38, 1.0e-40, float(np.float32(7.0 / 3.0))])
+def test_unusual_scales(gpu, scale):
+    """Zero, negative, overflowing and subnormal scales take the same rounding
+    path on both sides (bf16 of each scaled term, Inf and subnormals kept)."""
+    rng = np.random.default_rng(7)
+    sizes, bucket, D = [3000, 5000], 4000, 4
+    lay = OL.build_layout(sizes, bucket, D)
+    reps_h = [bf16_host(rng, lay.buffer_numel, 1.0) for _ in range(D)]
+    for r in range(D):
+        Ln = OL.shard_numel(lay, r)
+        st = [(rng.standard_normal(Ln) * 0.02).astype(np.float32), np.zeros(Ln, np.float32),
+              np.zeros(Ln, np.float32)]
+        run_rank_step(gpu, sizes, bucket, D, r, reps_h, st, scale, W.get("tiny").hp, 1, gpu.WORLD, gpu.WORLD)
+    free()
+
+
+def test_many_single_element_parameters(gpu):
+    """40,000 one-element parameters and a few larger ones: thousands of pieces
+    per rank, every chunk an edge of some piece but the runs coalesce."""
+    rng = np.random.default_rng(9)
+    sizes = [1] * 40000 + [4097, 1, 33, 1, 70000]
+    bucket, D = 9000, 8
+    lay = OL.build_layout(sizes, bucket, D)
+    reps_h = [bf16_host(rng, lay.buffer_numel, 1e-2) for _ in range(D)]
+    for r in (0, 5, 7):
+        Ln = OL.shard_numel(lay, r)
+        st = [(rng.standard_normal(Ln) * 0.02).astype(np.float32), (rng.standard_normal(Ln) * 1e-3).astype(np.float32),
+              ((rng.standard_normal(Ln) * 1e-3) ** 2).astype(np.float32)]
+        run_rank_step(gpu, sizes, bucket, D, r, reps_h, st, 0.125, W.get("tiny").hp, 4, gpu.LOCAL, gpu.WORLD)
+    free()

@@ -276,6 +276,25 @@ def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> d
                                    "achieved_gbps": gbps, "frac": gbps / PEAK_HBM_GBPS}
     log(f"reduce_scatter_local: {t * 1e6:.1f} us, {gbps:.0f} GB/s algorithmic")
     del red
+    # bucket by bucket: the same step launched once per bucket, last bucket
+    # first (the order a backward pass makes them ready), in one timed region
+    nb = int(plan.buckets().size)
+    st_b = [torch.zeros(plan.shard_numel, dtype=torch.float32, device=reps[0].device) for _ in range(3)]
+    par_b = torch.empty(plan.extent(coords), dtype=torch.int16, device=reps[0].device)
+    hp_b = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, step=1)
+
+    def per_bucket():
+        for b in reversed(range(nb)):
+            zdo.sharded_adam_step(plan, reps, coords, w.scale, *st_b, par_b, coords, stream=stream, buckets=(b, b + 1),
+                                  **hp_b)
+    t_b = timed(per_bucket)
+    gbps = plan.owned_numel * (2 * D + 26) / t_b / 1e9
+    out["bucket_by_bucket"] = {"buckets": nb, "total_us": t_b * 1e6, "achieved_gbps": gbps,
+                               "frac": gbps / PEAK_HBM_GBPS,
+                               "launches": "sharded_adam_step_buckets, one per bucket, last bucket first"}
+    log(f"bucket by bucket ({nb} launches): {t_b * 1e6:.1f} us, {gbps:.0f} GB/s algorithmic")
+    del st_b, par_b
+
     # global-norm clipping: the rank's squared norm (writing the reduced
     # gradient), the coefficient, the clipped step from the reduced gradient
     E = plan.owned_numel

@@ -181,6 +181,22 @@ int sharded_adam_step(const zdo_plan *plan, const uint16_t *const *grads, int32_
 int writeback_params(const zdo_plan *plan, const float *master, uint16_t *param_out,
                      int32_t param_coords, void *stream);
 
+/* ---- bucket by bucket ---------------------------------------------------------
+ * Page 1, §2 and §4.2: a bucket's collective starts as soon as the grads of
+ * its bucket are ready, bucket by bucket during the backward pass. These two
+ * calls do reduce_scatter_local's and sharded_adam_step's work for the
+ * buckets [bucket_begin, bucket_end) only (0 <= begin <= end <= number of
+ * buckets; an empty range does nothing). Calls over disjoint ranges that
+ * together cover every bucket, in any order, give the full call's results bit
+ * for bit. Other arguments and rules as the full calls. */
+int reduce_scatter_local_buckets(const zdo_plan *plan, int32_t bucket_begin, int32_t bucket_end,
+                                 const uint16_t *const *replicas, int32_t n_replicas, int32_t replica_coords,
+                                 float scale, uint16_t *out, int32_t out_coords, void *stream);
+int sharded_adam_step_buckets(const zdo_plan *plan, int32_t bucket_begin, int32_t bucket_end,
+                              const uint16_t *const *grads, int32_t n_grads, int32_t grad_coords, float scale,
+                              float *master, float *exp_avg, float *exp_avg_sq, uint16_t *param_out,
+                              int32_t param_coords, const zdo_adam *hp, float *main_grad_out, void *stream);
+
 /* ---- global-norm clipping ---------------------------------------------------
  * The distributed-training notes, §8.3: each rank's squared gradient sum is
  * all-reduced into the global norm sqrt(sum_i ||g_i||^2), and the gradients

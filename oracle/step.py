@@ -34,13 +34,17 @@ def _span(coords, world: L.Range, local_start: int):
 def rank_step(layout: L.Layout, rank: int, grads, grad_coords: int, scale: float,
               master: np.ndarray, m: np.ndarray, v: np.ndarray, hp_arr: np.ndarray,
               param_out: np.ndarray | None = None, param_coords: int = WORLD,
-              main_grad_out: np.ndarray | None = None, grad_coeff: float = 1.0) -> None:
+              main_grad_out: np.ndarray | None = None, grad_coeff: float = 1.0,
+              buckets: tuple | None = None) -> None:
     """Rank `rank`'s step, in place on master/m/v ([L] fp32) and param_out.
     grad_coeff multiplies the fp32 main grad (global-norm clipping); a NaN
-    coefficient means a skipped step: nothing changes."""
+    coefficient means a skipped step: nothing changes. buckets=(begin, end)
+    restricts the step to those buckets' pieces."""
     if np.isnan(grad_coeff):
         return
     for pc in L.rank_pieces(layout, rank):
+        if buckets is not None and not buckets[0] <= pc.bucket_index < buckets[1]:
+            continue
         k0 = pc.shard_offset
         k1 = k0 + pc.gbuf_world.size
         g0, g1 = _span(grad_coords, pc.gbuf_world, k0)
@@ -65,9 +69,12 @@ def rank_norm_sq(layout: L.Layout, rank: int, grads, grad_coords: int, scale: fl
 
 
 def reduce_scatter(layout: L.Layout, rank: int, grads, grad_coords: int, scale: float,
-                   out: np.ndarray, out_coords: int) -> None:
-    """The rank's whole range of every bucket (padding included), reduced into `out`."""
-    for world, base in L.rank_ranges(layout, rank):
+                   out: np.ndarray, out_coords: int, buckets: tuple | None = None) -> None:
+    """The rank's whole range of every bucket (padding included), reduced into
+    `out`; buckets=(begin, end) restricts it to those buckets."""
+    for b, (world, base) in enumerate(L.rank_ranges(layout, rank)):
+        if buckets is not None and not buckets[0] <= b < buckets[1]:
+            continue
         g0, g1 = _span(grad_coords, world, base)
         o0, o1 = _span(out_coords, world, base)
         N.reduce([g[g0:g1] for g in grads], scale, out=out[o0:o1])

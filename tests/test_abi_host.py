@@ -27,7 +27,7 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     L = Z.require_library()
     names = header_functions()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     assert sorted(Z.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -123,6 +123,9 @@ def test_launch_on_host_only_plan_is_an_error():
                                None) == Z.EHIP
     assert L.writeback_params(plan.handle, 64, 48, 0, None) == Z.EHIP
     assert L.grad_norm_sq(plan.handle, reps, 2, 0, 1.0, None, 0, 64, 128, None) == Z.EHIP
+    assert L.reduce_scatter_local_buckets(plan.handle, 0, 1, reps, 2, 0, 1.0, 48, 0, None) == Z.EHIP
+    assert L.sharded_adam_step_buckets(plan.handle, 0, 1, reps, 2, 0, 1.0, 64, 80, 96, None, 0, ctypes.byref(hp),
+                                       None, None) == Z.EHIP
     assert L.sharded_adam_step_clipped(plan.handle, reps, 2, 0, 1.0, 64, 80, 96, None, 0, ctypes.byref(hp), 112,
                                        None, None) == Z.EHIP
     assert b"device" in L.zdo_last_error()

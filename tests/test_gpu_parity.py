@@ -565,3 +565,80 @@ def test_many_single_element_parameters(gpu):
               ((rng.standard_normal(Ln) * 1e-3) ** 2).astype(np.float32)]
         run_rank_step(gpu, sizes, bucket, D, r, reps_h, st, 0.125, W.get("tiny").hp, 4, gpu.LOCAL, gpu.WORLD)
     free()
+
+
+# ---- bucket by bucket -------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["frag", "layout"])
+def test_bucket_ranges(gpu, name):
+    """Page 1, §2/§4.2: buckets handled one at a time as their grads become
+    ready. Per-bucket calls over every bucket, in reverse order, equal the full
+    call and the oracle bit for bit; a partial range touches its buckets only;
+    an empty range nothing; bad ranges are EINVAL."""
+    if name == "frag":
+        w = W.get("frag")
+        sizes, bucket, D, r = w.param_numel, w.bucket_numel, w.dp_size, 3
+        lay = OL.build_layout(sizes, bucket, D)
+        reps_d = _gen_world(w, lay.buffer_numel)
+        reps_h = [host_u16(x) for x in reps_d]
+    else:
+        rng = np.random.default_rng(77)
+        sizes, bucket, D, r = [3000, 1, 9000, 17, 4500, 2, 7000, 300, 11000], 6000, 4, 1
+        lay = OL.build_layout(sizes, bucket, D)
+        reps_h = [bf16_host(rng, lay.buffer_numel) for _ in range(D)]
+        reps_d = [to_dev(x) for x in reps_h]
+    plan = gpu.build_range_map(sizes, bucket, D, r)
+    nb = len(lay.buckets)
+    assert nb >= 3
+    N, Ln = plan.buffer_numel, plan.shard_numel
+    hp = W.get("tiny").hp
+    rng = np.random.default_rng(5)
+    st0 = [(rng.standard_normal(Ln) * 0.02).astype(np.float32), (rng.standard_normal(Ln) * 1e-3).astype(np.float32),
+           ((rng.standard_normal(Ln) * 1e-3) ** 2).astype(np.float32)]
+    scale = 1.0 / D
+
+    def run(ranges):
+        st = [to_dev(x) for x in st0]
+        par = torch.full((N,), SENTINEL, dtype=torch.int16, device=DEV)
+        for b0, b1 in ranges:
+            gpu.sharded_adam_step(plan, reps_d, gpu.WORLD, scale, *st, par, gpu.WORLD, buckets=(b0, b1),
+                                  **hp_kwargs(hp, 2))
+        return [host_f32(x) for x in st], host_u16(par)
+
+    def oracle(ranges):
+        st = [x.copy() for x in st0]
+        par = np.full(N, SENTINEL, np.uint16)
+        for b0, b1 in ranges:
+            OS.rank_step(lay, r, reps_h, OS.WORLD, scale, *st, ON.hp_array(hp, 2), par, OS.WORLD, buckets=(b0, b1))
+        return st, par
+
+    for ranges in ([(b, b + 1) for b in reversed(range(nb))], [(0, nb)], [(2, nb - 1)], [(1, 1)]):
+        got_st, got_par = run(ranges)
+        want_st, want_par = oracle(ranges)
+        for g, wv, nm in zip(got_st, want_st, ("master", "exp_avg", "exp_avg_sq")):
+            assert_f32(g, wv, f"{name} {ranges[:2]} {nm}")
+        assert_bf16(got_par, want_par, f"{name} {ranges[:2]} params")
+    # the full call equals the per-bucket calls
+    st = [to_dev(x) for x in st0]
+    par = torch.full((N,), SENTINEL, dtype=torch.int16, device=DEV)
+    gpu.sharded_adam_step(plan, reps_d, gpu.WORLD, scale, *st, par, gpu.WORLD, **hp_kwargs(hp, 2))
+    per_st, per_par = run([(b, b + 1) for b in reversed(range(nb))])
+    assert all(np.array_equal(host_f32(a).view(np.uint32), b.view(np.uint32)) for a, b in zip(st, per_st))
+    assert np.array_equal(host_u16(par), per_par)
+    # reduce-scatter in two halves, upper half first
+    out = torch.full((N,), SENTINEL, dtype=torch.int16, device=DEV)
+    gpu.reduce_scatter_local(plan, reps_d, gpu.WORLD, scale, out, gpu.WORLD, buckets=(nb // 2, nb))
+    gpu.reduce_scatter_local(plan, reps_d, gpu.WORLD, scale, out, gpu.WORLD, buckets=(0, nb // 2))
+    want = np.full(N, SENTINEL, np.uint16)
+    OS.reduce_scatter(lay, r, reps_h, OS.WORLD, scale, want, OS.WORLD)
+    assert_bf16(host_u16(out), want, f"{name} rs halves")
+    for bad in ((2, 1), (-1, 2), (0, nb + 1)):
+        with pytest.raises(gpu.ZdoError) as e:
+            gpu.sharded_adam_step(plan, reps_d, gpu.WORLD, scale, *st, par, gpu.WORLD, buckets=bad,
+                                  **hp_kwargs(hp, 2))
+        assert e.value.code == gpu.EINVAL
+        with pytest.raises(gpu.ZdoError) as e:
+            gpu.reduce_scatter_local(plan, reps_d, gpu.WORLD, scale, out, gpu.WORLD, buckets=bad)
+        assert e.value.code == gpu.EINVAL
+    del reps_d
+    free()

@@ -190,9 +190,9 @@ PY_MUTANTS = {
         ("k0 = pc.shard_offset\n        k1 = k0 + pc.gbuf_world.size\n        g0, g1 = _span(grad_coords",
          "k0 = pc.gbuf_local.start\n        k1 = k0 + pc.gbuf_world.size\n        g0, g1 = _span(grad_coords")]),
     "reduce-scatter over the parameter pieces only": ("step", [
-        ("    for world, base in L.rank_ranges(layout, rank):\n        g0, g1 = _span(grad_coords, world, base)",
-         "    for world, base in [(pc.gbuf_world, pc.shard_offset) for pc in L.rank_pieces(layout, rank)]:\n"
-         "        g0, g1 = _span(grad_coords, world, base)")]),
+        ("    for b, (world, base) in enumerate(L.rank_ranges(layout, rank)):",
+         "    for b, (world, base) in enumerate([(pc.gbuf_world, pc.shard_offset)\n"
+         "                                        for pc in L.rank_pieces(layout, rank)]):")]),
 }
 
 

@@ -236,3 +236,31 @@ def test_segmentation_invariance():
         for x, y in zip(a, b):
             assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
         assert np.array_equal(pa, pb)
+
+
+def test_bucket_ranges_compose_to_the_full_step():
+    # page 1, §2/§4.2: buckets are handled one at a time as they become ready;
+    # the per-bucket steps over a partition of the buckets, in any order, are the full step
+    lay = L.build_layout([300, 5, 70, 1000, 2, 640, 33], 350, 4)
+    assert len(lay.buckets) >= 4
+    rng = np.random.default_rng(12)
+    grads, master, m, v = make_inputs(lay, rng)
+    hp = N.hp_array(HP, 2)
+    nb = len(lay.buckets)
+    for r in range(4):
+        full = [S.gather_shard(lay, r, x) for x in (master, m, v)]
+        pf = np.full(lay.buffer_numel, 0x7FBF, np.uint16)
+        S.rank_step(lay, r, grads, S.WORLD, 0.25, *full, hp, pf, S.WORLD)
+        parts = [S.gather_shard(lay, r, x) for x in (master, m, v)]
+        pp = np.full(lay.buffer_numel, 0x7FBF, np.uint16)
+        for b in reversed(range(nb)):
+            S.rank_step(lay, r, grads, S.WORLD, 0.25, *parts, hp, pp, S.WORLD, buckets=(b, b + 1))
+        for x, y in zip(full, parts):
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+        assert np.array_equal(pf, pp)
+        rf = np.full(lay.buffer_numel, 0xFFFF, np.uint16)
+        S.reduce_scatter(lay, r, grads, S.WORLD, 0.25, rf, S.WORLD)
+        rp = np.full(lay.buffer_numel, 0xFFFF, np.uint16)
+        S.reduce_scatter(lay, r, grads, S.WORLD, 0.25, rp, S.WORLD, buckets=(nb // 2, nb))
+        S.reduce_scatter(lay, r, grads, S.WORLD, 0.25, rp, S.WORLD, buckets=(0, nb // 2))
+        assert np.array_equal(rf, rp)

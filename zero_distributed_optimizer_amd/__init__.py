@@ -66,8 +66,9 @@ BUCKET_DTYPE = np.dtype([("offset", "<i8"), ("numel", "<i8"), ("padded_numel", "
 EXPORTS = ("build_range_map", "zdo_plan_destroy", "zdo_plan_buffer_numel", "zdo_plan_shard_numel",
            "zdo_plan_owned_numel", "zdo_plan_dp_size", "zdo_plan_rank", "zdo_plan_buckets",
            "zdo_plan_pieces", "reduce_scatter_local", "force_all_reduce", "sharded_adam_step",
-           "writeback_params", "zdo_plan_norm_workspace_bytes", "grad_norm_sq", "clip_coefficient",
-           "sharded_adam_step_clipped", "zdo_device_copy", "zdo_last_error")
+           "writeback_params", "reduce_scatter_local_buckets", "sharded_adam_step_buckets",
+           "zdo_plan_norm_workspace_bytes", "grad_norm_sq", "clip_coefficient", "sharded_adam_step_clipped",
+           "zdo_device_copy", "zdo_last_error")
 
 _lib = None
 
@@ -97,6 +98,9 @@ def require_library() -> ctypes.CDLL:
     L.force_all_reduce.argtypes = [vp, vp, i32, f32, vp, vp]
     L.sharded_adam_step.argtypes = [vp, vp, i32, i32, f32, vp, vp, vp, vp, i32, ctypes.POINTER(Adam), vp, vp]
     L.writeback_params.argtypes = [vp, vp, vp, i32, vp]
+    L.reduce_scatter_local_buckets.argtypes = [vp, i32, i32, vp, i32, i32, f32, vp, i32, vp]
+    L.sharded_adam_step_buckets.argtypes = [vp, i32, i32, vp, i32, i32, f32, vp, vp, vp, vp, i32,
+                                            ctypes.POINTER(Adam), vp, vp]
     L.zdo_plan_norm_workspace_bytes.argtypes = [vp]
     L.zdo_plan_norm_workspace_bytes.restype = i64
     L.grad_norm_sq.argtypes = [vp, vp, i32, i32, f32, vp, i32, vp, vp, vp]
@@ -108,7 +112,8 @@ def require_library() -> ctypes.CDLL:
     L.zdo_last_error.restype = ctypes.c_char_p
     for f in ("build_range_map", "zdo_plan_buckets", "zdo_plan_pieces", "reduce_scatter_local",
               "force_all_reduce", "sharded_adam_step", "writeback_params", "grad_norm_sq", "clip_coefficient",
-              "sharded_adam_step_clipped", "zdo_device_copy"):
+              "sharded_adam_step_clipped", "reduce_scatter_local_buckets", "sharded_adam_step_buckets",
+              "zdo_device_copy"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -219,11 +224,16 @@ def _stream(stream, device) -> int:
 
 
 def reduce_scatter_local(plan: Plan, replicas, replica_coords: int, scale: float, out, out_coords: int,
-                         stream=None) -> None:
+                         stream=None, buckets=None) -> None:
+    """buckets=(begin, end): only those buckets (reduce_scatter_local_buckets)."""
     reps = _ptr_list(replicas, "replicas", plan.extent(replica_coords))
     o = _dev_ptr(out, "out", "bf16", plan.extent(out_coords))
-    _check(require_library().reduce_scatter_local(plan.handle, reps, len(replicas), replica_coords, scale, o,
-                                                  out_coords, _stream(stream, out.device)))
+    L, st = require_library(), _stream(stream, out.device)
+    if buckets is None:
+        _check(L.reduce_scatter_local(plan.handle, reps, len(replicas), replica_coords, scale, o, out_coords, st))
+    else:
+        _check(L.reduce_scatter_local_buckets(plan.handle, int(buckets[0]), int(buckets[1]), reps, len(replicas),
+                                              replica_coords, scale, o, out_coords, st))
 
 
 def force_all_reduce(plan: Plan, replicas, scale: float, out_full, stream=None) -> None:
@@ -239,7 +249,9 @@ def adam_hparams(lr: float, beta1: float, beta2: float, eps: float, weight_decay
 
 def sharded_adam_step(plan: Plan, grads, grad_coords: int, scale: float, master, exp_avg, exp_avg_sq,
                       param_out=None, param_coords: int = WORLD, *, lr: float, beta1: float, beta2: float,
-                      eps: float, weight_decay: float, step: int, main_grad_out=None, stream=None) -> None:
+                      eps: float, weight_decay: float, step: int, main_grad_out=None, stream=None,
+                      buckets=None) -> None:
+    """buckets=(begin, end): only those buckets (sharded_adam_step_buckets)."""
     L = plan.shard_numel
     g = _ptr_list(grads, "grads", plan.extent(grad_coords))
     m = _dev_ptr(master, "master", "f32", L)
@@ -248,9 +260,13 @@ def sharded_adam_step(plan: Plan, grads, grad_coords: int, scale: float, master,
     p = None if param_out is None else _dev_ptr(param_out, "param_out", "bf16", plan.extent(param_coords))
     mg = None if main_grad_out is None else _dev_ptr(main_grad_out, "main_grad_out", "f32", L)
     hp = adam_hparams(lr, beta1, beta2, eps, weight_decay, step)
-    _check(require_library().sharded_adam_step(plan.handle, g, len(grads), grad_coords, scale, m, a, s, p,
-                                               param_coords, ctypes.byref(hp), mg,
-                                               _stream(stream, master.device)))
+    L, st = require_library(), _stream(stream, master.device)
+    if buckets is None:
+        _check(L.sharded_adam_step(plan.handle, g, len(grads), grad_coords, scale, m, a, s, p, param_coords,
+                                   ctypes.byref(hp), mg, st))
+    else:
+        _check(L.sharded_adam_step_buckets(plan.handle, int(buckets[0]), int(buckets[1]), g, len(grads),
+                                           grad_coords, scale, m, a, s, p, param_coords, ctypes.byref(hp), mg, st))
 
 
 def sharded_adam_step_clipped(plan: Plan, grads, grad_coords: int, scale: float, master, exp_avg, exp_avg_sq,

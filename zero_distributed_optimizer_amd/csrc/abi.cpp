@@ -122,6 +122,33 @@ float bias_correction(float beta, int64_t t) {
     return float(1.0 - pw);
 }
 
+// Tiles [first, first + count) of a launch space that cover buckets [b0, b1):
+// segs are in bucket order, seg_bucket[i] is segment i's bucket (NULL: i).
+void bucket_tiles(const std::vector<Seg> &segs, const int32_t *seg_bucket, int64_t total_tiles, int32_t b0,
+                  int32_t b1, int64_t &first, int64_t &count) {
+    const int64_t n = int64_t(segs.size());
+    auto first_seg_at = [&](int32_t b) {
+        int64_t lo = 0, hi = n;   // first i with bucket(i) >= b
+        while (lo < hi) {
+            const int64_t mid = (lo + hi) / 2;
+            if ((seg_bucket ? seg_bucket[mid] : int32_t(mid)) < b)
+                lo = mid + 1;
+            else
+                hi = mid;
+        }
+        return lo < n ? segs[size_t(lo)].tile0 : total_tiles;
+    };
+    first = first_seg_at(b0);
+    count = first_seg_at(b1) - first;
+}
+
+int check_buckets(const zdo_plan *plan, int32_t b0, int32_t b1, const char *fn) {
+    if (b0 < 0 || b1 < b0 || b1 > int32_t(plan->buckets.size()))
+        return fail(ZDO_EINVAL, std::string(fn) + ": need 0 <= bucket_begin <= bucket_end <= " +
+                                    std::to_string(plan->buckets.size()));
+    return ZDO_OK;
+}
+
 }  // namespace
 
 void set_error(const std::string &msg) { g_error = msg; }
@@ -192,11 +219,9 @@ int zdo_plan_pieces(const zdo_plan *p, zdo_piece *out, int64_t cap, int64_t *n) 
     return ZDO_OK;
 }
 
-int reduce_scatter_local(const zdo_plan *plan, const uint16_t *const *replicas, int32_t n_replicas,
-                         int32_t replica_coords, float scale, uint16_t *out, int32_t out_coords, void *stream) {
-    const char *fn = "reduce_scatter_local";
-    if (int rc = check_plan(plan, fn))
-        return rc;
+static int reduce_scatter_impl(const char *fn, const zdo_plan *plan, int32_t b0, int32_t b1,
+                               const uint16_t *const *replicas, int32_t n_replicas, int32_t replica_coords,
+                               float scale, uint16_t *out, int32_t out_coords, void *stream) {
     if (n_replicas != plan->dp_size)
         return fail(ZDO_EINVAL, std::string(fn) + ": n_replicas must equal the DP size " +
                                     std::to_string(plan->dp_size));
@@ -215,13 +240,36 @@ int reduce_scatter_local(const zdo_plan *plan, const uint16_t *const *replicas, 
         if (overlap(so, spans[j]) && !(out == replicas[j] && out_coords == replica_coords))
             return fail(ZDO_EALIAS, std::string(fn) + ": out overlaps replica " + std::to_string(j) +
                                         " without coinciding with it");
-    a.walk = {plan->d_range_segs, plan->d_range_tile_seg, plan->range_tiles, 0, int64_t(plan->range_segs.size())};
+    int64_t first = 0, count = 0;
+    bucket_tiles(plan->range_segs, nullptr, plan->range_tiles, b0, b1, first, count);
+    a.walk = {plan->d_range_segs, plan->d_range_tile_seg, count, 0, int64_t(plan->range_segs.size()), first};
     a.nrep = n_replicas;
     a.in_local = replica_coords == ZDO_LOCAL;
     a.out_local = out_coords == ZDO_LOCAL;
     a.scale = scale;
     a.out = out;
     return launch_result(launch_reduce(a, plan->lds_per_cu, static_cast<hipStream_t>(stream)), fn);
+}
+
+int reduce_scatter_local(const zdo_plan *plan, const uint16_t *const *replicas, int32_t n_replicas,
+                         int32_t replica_coords, float scale, uint16_t *out, int32_t out_coords, void *stream) {
+    const char *fn = "reduce_scatter_local";
+    if (int rc = check_plan(plan, fn))
+        return rc;
+    return reduce_scatter_impl(fn, plan, 0, int32_t(plan->buckets.size()), replicas, n_replicas, replica_coords,
+                               scale, out, out_coords, stream);
+}
+
+int reduce_scatter_local_buckets(const zdo_plan *plan, int32_t bucket_begin, int32_t bucket_end,
+                                 const uint16_t *const *replicas, int32_t n_replicas, int32_t replica_coords,
+                                 float scale, uint16_t *out, int32_t out_coords, void *stream) {
+    const char *fn = "reduce_scatter_local_buckets";
+    if (int rc = check_plan(plan, fn))
+        return rc;
+    if (int rc = check_buckets(plan, bucket_begin, bucket_end, fn))
+        return rc;
+    return reduce_scatter_impl(fn, plan, bucket_begin, bucket_end, replicas, n_replicas, replica_coords, scale, out,
+                               out_coords, stream);
 }
 
 int force_all_reduce(const zdo_plan *plan, const uint16_t *const *replicas, int32_t n_replicas, float scale,
@@ -243,7 +291,7 @@ int force_all_reduce(const zdo_plan *plan, const uint16_t *const *replicas, int3
         if (overlap(so, spans[j]) && out_full != replicas[j])
             return fail(ZDO_EALIAS, std::string(fn) + ": out_full overlaps replica " + std::to_string(j) +
                                         " without coinciding with it");
-    a.walk = {nullptr, nullptr, seg_tiles(0, plan->buffer_numel), plan->buffer_numel, 0};
+    a.walk = {nullptr, nullptr, seg_tiles(0, plan->buffer_numel), plan->buffer_numel, 0, 0};
     a.nrep = n_replicas;
     a.in_local = 0;
     a.out_local = 0;
@@ -252,11 +300,15 @@ int force_all_reduce(const zdo_plan *plan, const uint16_t *const *replicas, int3
     return launch_result(launch_reduce(a, plan->lds_per_cu, static_cast<hipStream_t>(stream)), fn);
 }
 
-static int adam_step(const char *fn, const zdo_plan *plan, const uint16_t *const *grads, int32_t n_grads,
-                     int32_t grad_coords, float scale, float *master, float *exp_avg, float *exp_avg_sq,
-                     uint16_t *param_out, int32_t param_coords, const zdo_adam *hp, const float *coeff,
-                     float *main_grad_out, void *stream) {
+static int adam_step(const char *fn, const zdo_plan *plan, int32_t b0, int32_t b1, const uint16_t *const *grads,
+                     int32_t n_grads, int32_t grad_coords, float scale, float *master, float *exp_avg,
+                     float *exp_avg_sq, uint16_t *param_out, int32_t param_coords, const zdo_adam *hp,
+                     const float *coeff, float *main_grad_out, void *stream) {
     if (int rc = check_plan(plan, fn))
+        return rc;
+    if (b1 < 0)
+        b1 = int32_t(plan->buckets.size());
+    if (int rc = check_buckets(plan, b0, b1, fn))
         return rc;
     if (n_grads != plan->dp_size && n_grads != 1)
         return fail(ZDO_EINVAL, std::string(fn) + ": n_grads must be the DP size " + std::to_string(plan->dp_size) +
@@ -316,7 +368,9 @@ static int adam_step(const char *fn, const zdo_plan *plan, const uint16_t *const
         if (coeff && overlap(written[i].s, span_of(coeff, 1, 4)))
             return fail(ZDO_EALIAS, std::string(fn) + ": " + written[i].name + " overlaps grad_coeff");
     }
-    a.walk = {plan->d_param_segs, plan->d_param_tile_seg, plan->param_tiles, 0, int64_t(plan->param_segs.size())};
+    int64_t first = 0, count = 0;
+    bucket_tiles(plan->param_segs, plan->param_seg_bucket.data(), plan->param_tiles, b0, b1, first, count);
+    a.walk = {plan->d_param_segs, plan->d_param_tile_seg, count, 0, int64_t(plan->param_segs.size()), first};
     a.nrep = n_grads;
     a.in_local = grad_coords == ZDO_LOCAL;
     a.param_local = param_coords == ZDO_LOCAL;
@@ -342,8 +396,18 @@ static int adam_step(const char *fn, const zdo_plan *plan, const uint16_t *const
 int sharded_adam_step(const zdo_plan *plan, const uint16_t *const *grads, int32_t n_grads, int32_t grad_coords,
                       float scale, float *master, float *exp_avg, float *exp_avg_sq, uint16_t *param_out,
                       int32_t param_coords, const zdo_adam *hp, float *main_grad_out, void *stream) {
-    return adam_step("sharded_adam_step", plan, grads, n_grads, grad_coords, scale, master, exp_avg, exp_avg_sq,
-                     param_out, param_coords, hp, nullptr, main_grad_out, stream);
+    return adam_step("sharded_adam_step", plan, 0, -1, grads, n_grads, grad_coords, scale, master, exp_avg,
+                     exp_avg_sq, param_out, param_coords, hp, nullptr, main_grad_out, stream);
+}
+
+int sharded_adam_step_buckets(const zdo_plan *plan, int32_t bucket_begin, int32_t bucket_end,
+                              const uint16_t *const *grads, int32_t n_grads, int32_t grad_coords, float scale,
+                              float *master, float *exp_avg, float *exp_avg_sq, uint16_t *param_out,
+                              int32_t param_coords, const zdo_adam *hp, float *main_grad_out, void *stream) {
+    if (bucket_end < 0)
+        return fail(ZDO_EINVAL, "sharded_adam_step_buckets: bucket_end < 0");
+    return adam_step("sharded_adam_step_buckets", plan, bucket_begin, bucket_end, grads, n_grads, grad_coords, scale,
+                     master, exp_avg, exp_avg_sq, param_out, param_coords, hp, nullptr, main_grad_out, stream);
 }
 
 int sharded_adam_step_clipped(const zdo_plan *plan, const uint16_t *const *grads, int32_t n_grads,
@@ -352,7 +416,7 @@ int sharded_adam_step_clipped(const zdo_plan *plan, const uint16_t *const *grads
                               const float *grad_coeff, float *main_grad_out, void *stream) {
     if (!grad_coeff)
         return fail(ZDO_EINVAL, "sharded_adam_step_clipped: grad_coeff is NULL");
-    return adam_step("sharded_adam_step_clipped", plan, grads, n_grads, grad_coords, scale, master, exp_avg,
+    return adam_step("sharded_adam_step_clipped", plan, 0, -1, grads, n_grads, grad_coords, scale, master, exp_avg,
                      exp_avg_sq, param_out, param_coords, hp, grad_coeff, main_grad_out, stream);
 }
 
@@ -407,7 +471,7 @@ int grad_norm_sq(const zdo_plan *plan, const uint16_t *const *replicas, int32_t 
                 return fail(ZDO_EALIAS, std::string(fn) + ": reduced_out overlaps replica " + std::to_string(j) +
                                             " without coinciding with it");
     }
-    a.walk = {plan->d_param_segs, plan->d_param_tile_seg, plan->param_tiles, 0, int64_t(plan->param_segs.size())};
+    a.walk = {plan->d_param_segs, plan->d_param_tile_seg, plan->param_tiles, 0, int64_t(plan->param_segs.size()), 0};
     a.nrep = n_replicas;
     a.in_local = replica_coords == ZDO_LOCAL;
     a.out_local = out_coords == ZDO_LOCAL;
@@ -448,7 +512,7 @@ int writeback_params(const zdo_plan *plan, const float *master, uint16_t *param_
     if (overlap(span_of(master, plan->shard_numel, 4), span_of(param_out, extent(plan, param_coords), 2)))
         return fail(ZDO_EALIAS, std::string(fn) + ": param_out overlaps master");
     WritebackArgs a{};
-    a.walk = {plan->d_param_segs, plan->d_param_tile_seg, plan->param_tiles, 0, int64_t(plan->param_segs.size())};
+    a.walk = {plan->d_param_segs, plan->d_param_tile_seg, plan->param_tiles, 0, int64_t(plan->param_segs.size()), 0};
     a.param_local = param_coords == ZDO_LOCAL;
     a.master = master;
     a.param = param_out;

@@ -13,13 +13,15 @@ struct AdamConst {
 };
 
 // Segments walked by a launch: either a table (segs + per-tile segment
-// index) or, when segs is NULL, the single run [0, flat_numel).
+// index), of which the launch takes tiles [tile_begin, tile_begin + ntiles),
+// or, when segs is NULL, the single run [0, flat_numel).
 struct Walk {
     const Seg *segs;
     const uint32_t *tile_seg;
-    int64_t ntiles;
+    int64_t ntiles;      // tiles in this launch
     int64_t flat_numel;
     int64_t nseg;
+    int64_t tile_begin;  // first tile of this launch (a bucket range starts past 0)
 };
 
 struct ReduceArgs {

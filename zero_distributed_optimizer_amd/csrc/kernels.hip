@@ -168,7 +168,8 @@ __device__ __forceinline__ void adam(const AdamConst &c, float g, float &p, floa
 
 template <int D>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceArgs a) {
-    for (int64_t tile = blockIdx.x; tile < a.walk.ntiles; tile += gridDim.x) {
+    for (int64_t tile = a.walk.tile_begin + blockIdx.x; tile < a.walk.tile_begin + a.walk.ntiles;
+         tile += gridDim.x) {
         ChunkPos c;
         if (!chunk_of(a.walk, tile, c))
             continue;
@@ -202,7 +203,8 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a) {
         if (cf != cf)
             return;
     }
-    for (int64_t tile = blockIdx.x; tile < a.walk.ntiles; tile += gridDim.x) {
+    for (int64_t tile = a.walk.tile_begin + blockIdx.x; tile < a.walk.tile_begin + a.walk.ntiles;
+         tile += gridDim.x) {
         ChunkPos c;
         if (!chunk_of(a.walk, tile, c))
             continue;
@@ -282,7 +284,8 @@ static_assert(kBlock == 64, "the tile reduction below assumes one wave per workg
 
 template <int D>
 __global__ __launch_bounds__(kBlock) void norm_kernel(NormArgs a) {
-    for (int64_t tile = blockIdx.x; tile < a.walk.ntiles; tile += gridDim.x) {
+    for (int64_t tile = a.walk.tile_begin + blockIdx.x; tile < a.walk.tile_begin + a.walk.ntiles;
+         tile += gridDim.x) {
         ChunkPos c;
         double s = 0.0;
         if (chunk_of(a.walk, tile, c)) {
@@ -315,7 +318,7 @@ __global__ __launch_bounds__(kBlock) void norm_kernel(NormArgs a) {
         for (int off = 32; off > 0; off >>= 1)
             s = s + __shfl_xor(s, off, 64);
         if (threadIdx.x == 0)
-            a.partial[tile] = s;
+            a.partial[tile - a.walk.tile_begin] = s;
     }
 }
 
@@ -377,7 +380,8 @@ __global__ __launch_bounds__(64) void clip_kernel(const double *parts, int32_t n
 }
 
 __global__ __launch_bounds__(kBlock) void writeback_kernel(WritebackArgs a) {
-    for (int64_t tile = blockIdx.x; tile < a.walk.ntiles; tile += gridDim.x) {
+    for (int64_t tile = a.walk.tile_begin + blockIdx.x; tile < a.walk.tile_begin + a.walk.ntiles;
+         tile += gridDim.x) {
         ChunkPos c;
         if (!chunk_of(a.walk, tile, c))
             continue;

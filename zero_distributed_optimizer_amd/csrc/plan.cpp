@@ -117,8 +117,10 @@ int build_plan(const int64_t *param_numel, int32_t n_params, int64_t bucket_nume
         // Owned parameter elements of this bucket form one run (the padding
         // sits at the bucket's tail); the whole range is one run as well.
         const int64_t own_end = std::min(re, b.offset + b.numel);
-        if (own_end > rs)
+        if (own_end > rs) {
             p.param_segs.push_back({rs, b.shard_base, own_end - rs, 0});
+            p.param_seg_bucket.push_back(bi);
+        }
         p.range_segs.push_back({rs, b.shard_base, b.shard_numel, 0});
     }
     for (auto *segs : {&p.param_segs, &p.range_segs}) {

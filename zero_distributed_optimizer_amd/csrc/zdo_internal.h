@@ -51,6 +51,7 @@ struct zdo_plan {
     // Owned parameter elements (one run per bucket, padding excluded) and the
     // rank's whole range of every bucket (padding included).
     std::vector<zdo::Seg> param_segs, range_segs;
+    std::vector<int32_t> param_seg_bucket;   // bucket of each param seg (range seg i is bucket i)
     int64_t param_tiles = 0, range_tiles = 0;
     // Device copies, in one allocation on `device`: both segment lists and,
     // for every tile of each launch space, the index of its segment.

@@ -250,10 +250,14 @@ def main() -> int:
 
 
 def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> dict:
-    """The other two device calls on the same inputs: reduce_scatter_local over
-    the rank's whole ranges (2D + 2 bytes per element of the ranges) and, when
-    the replicas are whole buffers, force_all_reduce over the padded buffer
+    """The other device calls on the same inputs: reduce_scatter_local over
+    the rank's whole ranges (2D + 2 bytes per element of the ranges), the step
+    bucket by bucket, the clipped path, two instances composed (a
+    reduce-scatter within each, then the step on both results) and, when the
+    replicas are whole buffers, force_all_reduce over the padded buffer
     (2D + 2 bytes per buffer element). HIP events around each launch."""
+    import workloads as W
+
     D = plan.dp_size
     out = {}
 
@@ -324,6 +328,37 @@ def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> d
     log(f"clipped step: norm {t_norm * 1e6:.1f} us + clip {t_clip * 1e6:.1f} us + step {t_step * 1e6:.1f} us, "
         f"{out['clipped_step']['achieved_gbps']:.0f} GB/s algorithmic")
     del ws, red, st, par
+
+    # two instances of D ranks: a reduce-scatter within each instance (the
+    # bench's replicas, and D more in local coordinates), then the step on the
+    # two results with scale 1, which sums them as the all-reduce across
+    # instances does
+    n_inst = 2
+    Ln = plan.shard_numel
+    extra = torch.empty(D * ((Ln + 7) // 8 * 8), dtype=torch.bfloat16, device=dev)
+    inst1 = []
+    for j in range(D):
+        s = extra[j * ((Ln + 7) // 8 * 8): j * ((Ln + 7) // 8 * 8) + Ln]
+        W.normal_bf16(Ln, w.grad_sigma, W.seed(w.cfg, 1, "grad", j), out=s)
+        inst1.append(s.view(torch.int16))
+    rs = [torch.empty(Ln, dtype=torch.int16, device=dev) for _ in range(n_inst)]
+    st = [torch.zeros(Ln, dtype=torch.float32, device=dev) for _ in range(3)]
+    par = torch.empty(plan.extent(coords), dtype=torch.int16, device=dev)
+    t_rs0 = timed(lambda: zdo.reduce_scatter_local(plan, reps, coords, w.scale / n_inst, rs[0], zdo.LOCAL, stream))
+    t_rs1 = timed(lambda: zdo.reduce_scatter_local(plan, inst1, zdo.LOCAL, w.scale / n_inst, rs[1], zdo.LOCAL,
+                                                   stream))
+    t_st = timed(lambda: zdo.sharded_adam_step(plan, rs, zdo.LOCAL, 1.0, *st, par, coords, stream=stream, **hp))
+    t_all = t_rs0 + t_rs1 + t_st
+    bytes_all = n_inst * ranges * (2 * D + 2) + E * (2 * n_inst + 26)
+    out["two_level_instances"] = {
+        "path": f"reduce_scatter_local within each of {n_inst} instances of D ranks, then sharded_adam_step on "
+                f"the {n_inst} results (scale 1)",
+        "instances": n_inst, "rs_us": [t_rs0 * 1e6, t_rs1 * 1e6], "step_us": t_st * 1e6, "total_us": t_all * 1e6,
+        "algorithmic_bytes": bytes_all, "achieved_gbps": bytes_all / t_all / 1e9,
+        "frac": bytes_all / t_all / 1e9 / PEAK_HBM_GBPS, "step_gbps": E * (2 * n_inst + 26) / t_st / 1e9}
+    log(f"two-level, {n_inst} instances: rs {t_rs0 * 1e6:.1f} + {t_rs1 * 1e6:.1f} us + step {t_st * 1e6:.1f} us, "
+        f"{out['two_level_instances']['achieved_gbps']:.0f} GB/s algorithmic")
+    del extra, inst1, rs, st, par
 
     if coords == zdo.WORLD:
         N = plan.buffer_numel

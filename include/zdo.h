@@ -28,6 +28,16 @@
  *     memory and never synchronise the host.
  *   - Coordinates of a buffer: ZDO_WORLD indexes the whole padded buffer
  *     [0, N); ZDO_LOCAL indexes the rank's shard [0, L).
+ *   - The contributions a call sums (n_replicas / n_grads, 1..ZDO_MAX_REPLICAS,
+ *     each a device pointer in a host array) are summed in the order given.
+ *     The plain step passes the D ranks' contributions. With several
+ *     distributed-optimizer instances (page 1, §5: the reduce-scatter runs
+ *     within each instance of D ranks, then an all-reduce across the
+ *     instances), call reduce_scatter_local once per instance on its D
+ *     contributions, then pass the instances' results, in instance order and
+ *     with scale 1, as the contributions of sharded_adam_step (or of
+ *     reduce_scatter_local for the reduced gradient alone); one contribution
+ *     with scale 1 is an already reduced gradient, taken as it is.
  *   - Every call returns ZDO_OK (0) or a negative ZDO_E* code; the message of
  *     the last failing call on this thread is zdo_last_error(). No call
  *     aborts or throws. Faults inside a kernel surface when the caller
@@ -136,8 +146,9 @@ int zdo_plan_pieces(const zdo_plan *plan, zdo_piece *out, int64_t cap, int64_t *
 
 /* Reduce-scatter of the D contributions over the rank's whole range of every
  * bucket, padding included (page 1, §4.2, with the scaling of §5 first).
- * replicas: host array of n_replicas (== D) device pointers, each a bf16
- * buffer of N (replica_coords = ZDO_WORLD) or L (ZDO_LOCAL) elements.
+ * replicas: host array of n_replicas device pointers (the D ranks'
+ * contributions, or see the instances rule above), each a bf16 buffer of N
+ * (replica_coords = ZDO_WORLD) or L (ZDO_LOCAL) elements.
  * out: bf16, N elements (out_coords = ZDO_WORLD) or L (ZDO_LOCAL); only the
  * rank's ranges are written. out may coincide exactly with one replica when
  * both use the same coordinates (in place, like a reduce-scatter into the
@@ -149,7 +160,7 @@ int reduce_scatter_local(const zdo_plan *plan, const uint16_t *const *replicas, 
 /* All-reduce of the D contributions over the whole padded buffer (page 1, §5,
  * force_all_reduce: the full reduced grads instead of the rank's share).
  * Same arithmetic as reduce_scatter_local; independent of the rank.
- * replicas: n_replicas (== D) device bf16 buffers of N elements. out_full:
+ * replicas: n_replicas device bf16 buffers of N elements. out_full:
  * bf16, N elements; it may coincide exactly with one replica. */
 int force_all_reduce(const zdo_plan *plan, const uint16_t *const *replicas, int32_t n_replicas,
                      float scale, uint16_t *out_full, void *stream);
@@ -159,10 +170,11 @@ int force_all_reduce(const zdo_plan *plan, const uint16_t *const *replicas, int3
  * range map, Adam on master/exp_avg/exp_avg_sq, and write bf16(master') into
  * param_out (page 1, §4.2, §4.3, §5). Padding and elements of other ranks
  * are neither read from the state nor written anywhere.
- * grads: host array of n_grads device pointers; n_grads == D (the replicas)
- * or 1 (an already reduced buffer, e.g. the output of reduce_scatter_local
- * or force_all_reduce, with scale 1 to leave it unchanged), bf16 of N
- * (grad_coords ZDO_WORLD) or L (ZDO_LOCAL) elements.
+ * grads: host array of n_grads device pointers: the D replicas, or 1 already
+ * reduced buffer (e.g. the output of reduce_scatter_local or
+ * force_all_reduce, with scale 1 to leave it unchanged), or the instances'
+ * reduce-scatter results (see above); bf16 of N (grad_coords ZDO_WORLD) or
+ * L (ZDO_LOCAL) elements.
  * master, exp_avg, exp_avg_sq: fp32, L elements each (LOCAL), updated in
  * place; pairwise disjoint. param_out: bf16, N (param_coords ZDO_WORLD) or L
  * (ZDO_LOCAL) elements, or NULL to skip the write-back. main_grad_out: fp32,
@@ -220,8 +232,7 @@ int64_t zdo_plan_norm_workspace_bytes(const zdo_plan *plan);
  * 1024 contiguous runs, then the runs) into *norm_sq_out. The order
  * depends only on the plan, so the result is bit-identical run to run;
  * against a sequential fp64 sum it differs only by fp64 rounding.
- * replicas / n_replicas / replica_coords: as sharded_adam_step's grads
- * (n_replicas = D, or 1 for an already reduced buffer with scale 1).
+ * replicas / n_replicas / replica_coords: as sharded_adam_step's grads.
  * reduced_out: NULL, or bf16 N (out_coords ZDO_WORLD) / L (ZDO_LOCAL)
  * elements receiving g at the owned elements only (then sharded_adam_step
  * with n_grads = 1 and scale 1 on it reads 2 bytes per element instead of

@@ -339,7 +339,7 @@ def test_error_paths(gpu):
     h = torch.zeros(256, dtype=torch.float32, device=DEV)
     hp = hp_kwargs(W.get("tiny").hp, 1)
     with pytest.raises(Z.ZdoError) as e:
-        Z.reduce_scatter_local(plan, [x], Z.WORLD, 1.0, x, Z.WORLD)           # one replica, D = 2
+        Z.reduce_scatter_local(plan, [x] * 65, Z.WORLD, 1.0, x, Z.WORLD)      # more than 64 contributions
     assert e.value.code == Z.EINVAL
     with pytest.raises(Z.ZdoError) as e:
         Z.reduce_scatter_local(plan, [x, x], Z.WORLD, 1.0, x[8:], Z.WORLD)    # partial overlap
@@ -354,7 +354,7 @@ def test_error_paths(gpu):
         Z.sharded_adam_step(plan, [x, x], Z.WORLD, 1.0, f[1:], g, h, None, **hp)   # misaligned
     assert e.value.code == Z.EALIGN
     with pytest.raises(Z.ZdoError) as e:
-        Z.sharded_adam_step(plan, [x, x, x], Z.WORLD, 1.0, f, g, h, None, **hp)    # 3 grads at D = 2
+        Z.sharded_adam_step(plan, [], Z.WORLD, 1.0, f, g, h, None, **hp)           # no contribution
     assert e.value.code == Z.EINVAL
     with pytest.raises(Z.ZdoError) as e:
         Z.sharded_adam_step(plan, [x, x], Z.WORLD, 1.0, f, g, h, x, Z.WORLD, **dict(hp, step=0))
@@ -641,4 +641,63 @@ def test_bucket_ranges(gpu, name):
             gpu.reduce_scatter_local(plan, reps_d, gpu.WORLD, scale, out, gpu.WORLD, buckets=bad)
         assert e.value.code == gpu.EINVAL
     del reps_d
+    free()
+
+
+# ---- several distributed-optimizer instances ----------------------------------------------
+
+@pytest.mark.parametrize("D,n_inst", [(4, 2), (8, 4), (2, 3), (16, 2)])
+def test_two_level_instances(gpu, D, n_inst):
+    """Page 1, §5: the reduce-scatter runs within each instance of D ranks and
+    an all-reduce across the n_inst instances follows. On the GPU: one
+    reduce_scatter_local per instance, then the step (and the reduced gradient
+    alone) on the instances' results with scale 1; against the oracle's same
+    composition, bit for bit."""
+    rng = np.random.default_rng(100 * D + n_inst)
+    sizes, bucket = [5000, 13, 20000, 1, 4097, 2200], 9000
+    lay = OL.build_layout(sizes, bucket, D)
+    N = lay.buffer_numel
+    reps_h = [[bf16_host(rng, N) for _ in range(D)] for _ in range(n_inst)]
+    reps_d = [[to_dev(x) for x in inst] for inst in reps_h]
+    scale = 1.0 / (D * n_inst)
+    hp = W.get("tiny").hp
+    for r in sorted({0, D - 1, int(rng.integers(D))}):
+        plan = gpu.build_range_map(sizes, bucket, D, r)
+        Ln = plan.shard_numel
+        rs_d, rs_h = [], []
+        for i in range(n_inst):
+            out = torch.zeros(Ln, dtype=torch.int16, device=DEV)
+            gpu.reduce_scatter_local(plan, reps_d[i], gpu.WORLD, scale, out, gpu.LOCAL)
+            rs_d.append(out)
+            want = np.zeros(Ln, np.uint16)
+            OS.reduce_scatter(lay, r, reps_h[i], OS.WORLD, scale, want, OS.LOCAL)
+            rs_h.append(want)
+            assert_bf16(host_u16(out), want, f"instance {i} rs")
+        red = torch.zeros(Ln, dtype=torch.int16, device=DEV)
+        gpu.reduce_scatter_local(plan, rs_d, gpu.LOCAL, 1.0, red, gpu.LOCAL)
+        want_red = np.zeros(Ln, np.uint16)
+        OS.reduce_scatter(lay, r, rs_h, OS.LOCAL, 1.0, want_red, OS.LOCAL)
+        assert_bf16(host_u16(red), want_red, "all-reduce across instances")
+        # the step on the instances' results, against the oracle's step on them
+        state_h = [(rng.standard_normal(Ln) * 0.02).astype(np.float32),
+                   (rng.standard_normal(Ln) * 1e-3).astype(np.float32),
+                   ((rng.standard_normal(Ln) * 1e-3) ** 2).astype(np.float32)]
+        master, m, v = (to_dev(x) for x in state_h)
+        par = torch.full((max(N, 8),), SENTINEL, dtype=torch.int16, device=DEV)
+        mg = torch.full((max(Ln, 8),), -7.0, dtype=torch.float32, device=DEV)
+        gpu.sharded_adam_step(plan, rs_d, gpu.LOCAL, 1.0, master, m, v, par, gpu.WORLD, main_grad_out=mg,
+                              **hp_kwargs(hp, 3))
+        want = [x.copy() for x in state_h]
+        want_par = np.full(max(N, 8), SENTINEL, np.uint16)
+        want_mg = np.full(max(Ln, 8), -7.0, np.float32)
+        OS.rank_step(lay, r, rs_h, OS.LOCAL, 1.0, *want, ON.hp_array(hp, 3), want_par, OS.WORLD, want_mg[:Ln])
+        for got, w, name in zip((master, m, v), want, ("master", "exp_avg", "exp_avg_sq")):
+            assert_f32(host_f32(got), w, f"{name} r={r}")
+        assert_bf16(host_u16(par), want_par, f"params r={r}")
+        assert_f32(host_f32(mg), want_mg, f"main grad r={r}")
+        # on the owned elements the main grad is the widened all-reduced gradient
+        own = np.zeros(Ln, bool)
+        for pc in OL.rank_pieces(lay, r):
+            own[pc.shard_offset:pc.shard_offset + pc.gbuf_world.size] = True
+        assert_f32(host_f32(mg)[:Ln][own], ON.widen(want_red)[own], "main grad = widen(all-reduce)")
     free()

@@ -264,3 +264,56 @@ def test_bucket_ranges_compose_to_the_full_step():
         S.reduce_scatter(lay, r, grads, S.WORLD, 0.25, rp, S.WORLD, buckets=(nb // 2, nb))
         S.reduce_scatter(lay, r, grads, S.WORLD, 0.25, rp, S.WORLD, buckets=(0, nb // 2))
         assert np.array_equal(rf, rp)
+
+
+def test_two_level_reduction_of_instances():
+    """Page 1, §5: with several distributed-optimizer instances, the
+    reduce-scatter runs within each instance and an all-reduce across the
+    instances follows. Reading: each instance's bf16 reduce-scatter result,
+    summed over instances in instance order (fp32, one rounding)."""
+    D, n_inst = 4, 3
+    lay = L.build_layout([700, 9, 1300, 64], 900, D)
+    rng = np.random.default_rng(13)
+    reps = [[bf16(rng.standard_normal(lay.buffer_numel) * 1e-2) for _ in range(D)] for _ in range(n_inst)]
+    hp = N.hp_array(HP, 1)
+    for r in range(D):
+        rs = []
+        for i in range(n_inst):
+            out = np.zeros(L.shard_numel(lay, r), np.uint16)
+            S.reduce_scatter(lay, r, reps[i], S.WORLD, 0.125, out, S.LOCAL)
+            rs.append(out)
+        # the all-reduce across instances over the rank's range
+        red = np.zeros(L.shard_numel(lay, r), np.uint16)
+        S.reduce_scatter(lay, r, rs, S.LOCAL, 1.0, red, S.LOCAL)
+        # element by element, bf16(sum_i bf16(sum_j bf16(s g_ij))) evaluated
+        # again with numpy float32 operations, apart from the C arithmetic
+        for pc in L.rank_pieces(lay, r)[:3]:
+            for e in range(0, pc.gbuf_world.size, 37):
+                w_ = pc.gbuf_world.start + e
+                k = pc.shard_offset + e
+                total = 0.0
+                for i in range(n_inst):
+                    inner = np.float32(0.0)
+                    for j in range(D):
+                        t = N.widen(N.narrow(np.array([N.widen(reps[i][j][w_:w_ + 1])[0] * np.float32(0.125)],
+                                                      np.float32)))[0]
+                        inner = np.float32(inner + t) if j else t
+                    total = np.float32(total + N.widen(N.narrow(np.array([inner], np.float32)))[0]) if i else \
+                        N.widen(N.narrow(np.array([inner], np.float32)))[0]
+                assert red[k] == N.narrow(np.array([total], np.float32))[0]
+        # one instance: the two levels are the plain reduce-scatter
+        one = np.zeros(L.shard_numel(lay, r), np.uint16)
+        S.reduce_scatter(lay, r, [rs[0]], S.LOCAL, 1.0, one, S.LOCAL)
+        assert np.array_equal(one, rs[0])
+        # the step on the instances' results (n contributions, scale 1) is the
+        # step on the two-level reduced gradient
+        a = [S.gather_shard(lay, r, x) for x in (np.zeros(lay.buffer_numel, np.float32),) * 3]
+        b = [x.copy() for x in a]
+        S.rank_step(lay, r, rs, S.LOCAL, 1.0, *a, hp)
+        S.rank_step(lay, r, [red], S.LOCAL, 1.0, *b, hp)
+        for x, y in zip(a, b):
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    # two levels differ from one flat sum over all D * n_inst contributions on some elements
+    flat = S.all_reduce([x for inst in reps for x in inst], 0.125)
+    two = [S.all_reduce(inst, 0.125) for inst in reps]
+    assert (S.all_reduce(two, 1.0) != flat).any()

@@ -222,9 +222,9 @@ int zdo_plan_pieces(const zdo_plan *p, zdo_piece *out, int64_t cap, int64_t *n) 
 static int reduce_scatter_impl(const char *fn, const zdo_plan *plan, int32_t b0, int32_t b1,
                                const uint16_t *const *replicas, int32_t n_replicas, int32_t replica_coords,
                                float scale, uint16_t *out, int32_t out_coords, void *stream) {
-    if (n_replicas != plan->dp_size)
-        return fail(ZDO_EINVAL, std::string(fn) + ": n_replicas must equal the DP size " +
-                                    std::to_string(plan->dp_size));
+    if (n_replicas < 1 || n_replicas > ZDO_MAX_REPLICAS)
+        return fail(ZDO_EINVAL, std::string(fn) + ": n_replicas must be in [1, " + std::to_string(ZDO_MAX_REPLICAS) +
+                                    "]");
     if (int rc = check_coords(replica_coords, fn, "replica_coords"))
         return rc;
     if (int rc = check_coords(out_coords, fn, "out_coords"))
@@ -277,9 +277,9 @@ int force_all_reduce(const zdo_plan *plan, const uint16_t *const *replicas, int3
     const char *fn = "force_all_reduce";
     if (int rc = check_plan(plan, fn))
         return rc;
-    if (n_replicas != plan->dp_size)
-        return fail(ZDO_EINVAL, std::string(fn) + ": n_replicas must equal the DP size " +
-                                    std::to_string(plan->dp_size));
+    if (n_replicas < 1 || n_replicas > ZDO_MAX_REPLICAS)
+        return fail(ZDO_EINVAL, std::string(fn) + ": n_replicas must be in [1, " + std::to_string(ZDO_MAX_REPLICAS) +
+                                    "]");
     ReduceArgs a{};
     Span spans[ZDO_MAX_REPLICAS];
     if (int rc = take_replicas(plan, replicas, n_replicas, ZDO_WORLD, fn, a.rep, spans))
@@ -310,9 +310,9 @@ static int adam_step(const char *fn, const zdo_plan *plan, int32_t b0, int32_t b
         b1 = int32_t(plan->buckets.size());
     if (int rc = check_buckets(plan, b0, b1, fn))
         return rc;
-    if (n_grads != plan->dp_size && n_grads != 1)
-        return fail(ZDO_EINVAL, std::string(fn) + ": n_grads must be the DP size " + std::to_string(plan->dp_size) +
-                                    " or 1 (pre-reduced)");
+    if (n_grads < 1 || n_grads > ZDO_MAX_REPLICAS)
+        return fail(ZDO_EINVAL, std::string(fn) + ": n_grads must be in [1, " + std::to_string(ZDO_MAX_REPLICAS) +
+                                    "]");
     if (int rc = check_coords(grad_coords, fn, "grad_coords"))
         return rc;
     if (param_out)
@@ -433,9 +433,9 @@ int grad_norm_sq(const zdo_plan *plan, const uint16_t *const *replicas, int32_t 
     const char *fn = "grad_norm_sq";
     if (int rc = check_plan(plan, fn))
         return rc;
-    if (n_replicas != plan->dp_size && n_replicas != 1)
-        return fail(ZDO_EINVAL, std::string(fn) + ": n_replicas must be the DP size " +
-                                    std::to_string(plan->dp_size) + " or 1 (pre-reduced)");
+    if (n_replicas < 1 || n_replicas > ZDO_MAX_REPLICAS)
+        return fail(ZDO_EINVAL, std::string(fn) + ": n_replicas must be in [1, " + std::to_string(ZDO_MAX_REPLICAS) +
+                                    "]");
     if (int rc = check_coords(replica_coords, fn, "replica_coords"))
         return rc;
     if (reduced_out)

@@ -252,10 +252,11 @@ def main() -> int:
 def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> dict:
     """The other device calls on the same inputs: reduce_scatter_local over
     the rank's whole ranges (2D + 2 bytes per element of the ranges), the step
-    bucket by bucket, the clipped path, two instances composed (a
-    reduce-scatter within each, then the step on both results) and, when the
-    replicas are whole buffers, force_all_reduce over the padded buffer
-    (2D + 2 bytes per buffer element). HIP events around each launch."""
+    bucket by bucket, the clipped path, two instances (composed from a
+    reduce-scatter within each and the step on both results, and in one
+    pass) and, when the replicas are whole buffers, force_all_reduce over the
+    padded buffer (2D + 2 bytes per buffer element). HIP events around each
+    launch."""
     import workloads as W
 
     D = plan.dp_size
@@ -329,36 +330,51 @@ def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> d
         f"{out['clipped_step']['achieved_gbps']:.0f} GB/s algorithmic")
     del ws, red, st, par
 
-    # two instances of D ranks: a reduce-scatter within each instance (the
-    # bench's replicas, and D more in local coordinates), then the step on the
-    # two results with scale 1, which sums them as the all-reduce across
-    # instances does
+    # two instances of D ranks: the bench's replicas and D more in the same
+    # coordinates. Composed: a reduce-scatter within each instance, then the
+    # step on the two results with scale 1 (which sums them as the all-reduce
+    # across instances does). One pass: sharded_adam_step_instances.
     n_inst = 2
     Ln = plan.shard_numel
-    extra = torch.empty(D * ((Ln + 7) // 8 * 8), dtype=torch.bfloat16, device=dev)
-    inst1 = []
-    for j in range(D):
-        s = extra[j * ((Ln + 7) // 8 * 8): j * ((Ln + 7) // 8 * 8) + Ln]
-        W.normal_bf16(Ln, w.grad_sigma, W.seed(w.cfg, 1, "grad", j), out=s)
-        inst1.append(s.view(torch.int16))
-    rs = [torch.empty(Ln, dtype=torch.int16, device=dev) for _ in range(n_inst)]
-    st = [torch.zeros(Ln, dtype=torch.float32, device=dev) for _ in range(3)]
-    par = torch.empty(plan.extent(coords), dtype=torch.int16, device=dev)
-    t_rs0 = timed(lambda: zdo.reduce_scatter_local(plan, reps, coords, w.scale / n_inst, rs[0], zdo.LOCAL, stream))
-    t_rs1 = timed(lambda: zdo.reduce_scatter_local(plan, inst1, zdo.LOCAL, w.scale / n_inst, rs[1], zdo.LOCAL,
-                                                   stream))
-    t_st = timed(lambda: zdo.sharded_adam_step(plan, rs, zdo.LOCAL, 1.0, *st, par, coords, stream=stream, **hp))
-    t_all = t_rs0 + t_rs1 + t_st
-    bytes_all = n_inst * ranges * (2 * D + 2) + E * (2 * n_inst + 26)
-    out["two_level_instances"] = {
-        "path": f"reduce_scatter_local within each of {n_inst} instances of D ranks, then sharded_adam_step on "
-                f"the {n_inst} results (scale 1)",
-        "instances": n_inst, "rs_us": [t_rs0 * 1e6, t_rs1 * 1e6], "step_us": t_st * 1e6, "total_us": t_all * 1e6,
-        "algorithmic_bytes": bytes_all, "achieved_gbps": bytes_all / t_all / 1e9,
-        "frac": bytes_all / t_all / 1e9 / PEAK_HBM_GBPS, "step_gbps": E * (2 * n_inst + 26) / t_st / 1e9}
-    log(f"two-level, {n_inst} instances: rs {t_rs0 * 1e6:.1f} + {t_rs1 * 1e6:.1f} us + step {t_st * 1e6:.1f} us, "
-        f"{out['two_level_instances']['achieved_gbps']:.0f} GB/s algorithmic")
-    del extra, inst1, rs, st, par
+    n_rep = plan.extent(coords)
+    stride = (n_rep + 7) // 8 * 8
+    need = 2 * D * stride + 2 * n_inst * Ln + 12 * Ln + 2 * n_rep + (1 << 30)
+    if torch.cuda.mem_get_info(dev)[0] < need:
+        out["two_level_instances"] = {"skipped": "not enough free device memory for a second instance"}
+        log("two-level instances: skipped (device memory)")
+    else:
+        extra = torch.empty(D * stride, dtype=torch.bfloat16, device=dev)
+        inst1 = []
+        for j in range(D):
+            s = extra[j * stride: j * stride + n_rep]
+            W.normal_bf16(n_rep, w.grad_sigma, W.seed(w.cfg, 1, "grad", j), out=s)
+            inst1.append(s.view(torch.int16))
+        rs = [torch.empty(Ln, dtype=torch.int16, device=dev) for _ in range(n_inst)]
+        st = [torch.zeros(Ln, dtype=torch.float32, device=dev) for _ in range(3)]
+        par = torch.empty(n_rep, dtype=torch.int16, device=dev)
+        s_i = w.scale / n_inst
+        t_rs0 = timed(lambda: zdo.reduce_scatter_local(plan, reps, coords, s_i, rs[0], zdo.LOCAL, stream))
+        t_rs1 = timed(lambda: zdo.reduce_scatter_local(plan, inst1, coords, s_i, rs[1], zdo.LOCAL, stream))
+        t_st = timed(lambda: zdo.sharded_adam_step(plan, rs, zdo.LOCAL, 1.0, *st, par, coords, stream=stream, **hp))
+        t_one = timed(lambda: zdo.sharded_adam_step_instances(plan, [reps, inst1], coords, s_i, *st, par, coords,
+                                                              stream=stream, **hp))
+        t_all = t_rs0 + t_rs1 + t_st
+        bytes_all = n_inst * ranges * (2 * D + 2) + E * (2 * n_inst + 26)
+        bytes_one = E * (2 * n_inst * D + 26)
+        out["two_level_instances"] = {
+            "instances": n_inst,
+            "composed": {"path": f"reduce_scatter_local within each of {n_inst} instances of D ranks, then "
+                                 f"sharded_adam_step on the {n_inst} results (scale 1)",
+                         "rs_us": [t_rs0 * 1e6, t_rs1 * 1e6], "step_us": t_st * 1e6, "total_us": t_all * 1e6,
+                         "algorithmic_bytes": bytes_all, "achieved_gbps": bytes_all / t_all / 1e9,
+                         "frac": bytes_all / t_all / 1e9 / PEAK_HBM_GBPS},
+            "one_pass": {"path": "sharded_adam_step_instances", "bytes_per_element": 2 * n_inst * D + 26,
+                         "kernel_avg_us": t_one * 1e6, "achieved_gbps": bytes_one / t_one / 1e9,
+                         "frac": bytes_one / t_one / 1e9 / PEAK_HBM_GBPS, "elements_per_s": E / t_one}}
+        log(f"two-level, {n_inst} instances: composed rs {t_rs0 * 1e6:.1f} + {t_rs1 * 1e6:.1f} us + step "
+            f"{t_st * 1e6:.1f} us ({bytes_all / t_all / 1e9:.0f} GB/s); one pass {t_one * 1e6:.1f} us "
+            f"({bytes_one / t_one / 1e9:.0f} GB/s)")
+        del extra, inst1, rs, st, par
 
     if coords == zdo.WORLD:
         N = plan.buffer_numel

@@ -186,6 +186,24 @@ int sharded_adam_step(const zdo_plan *plan, const uint16_t *const *grads, int32_
                       float *exp_avg_sq, uint16_t *param_out, int32_t param_coords,
                       const zdo_adam *hp, float *main_grad_out, void *stream);
 
+/* sharded_adam_step for n_instances distributed-optimizer instances of D
+ * ranks each, in one pass (page 1, §5: the reduce-scatter runs within each
+ * instance, then an all-reduce across the instances). grads: host array of
+ * n_instances * D device pointers, instance-major (instance i's D
+ * contributions, in rank order, at [i*D, i*D + D)), all in grad_coords.
+ * Each instance's contributions are summed as sharded_adam_step sums them
+ * (scale applied to each term first) and rounded to bf16; those n_instances
+ * bf16 sums are added in fp32 in instance order and rounded to bf16, and the
+ * step continues as sharded_adam_step. The result equals reduce_scatter_local
+ * per instance followed by sharded_adam_step on the instance results with
+ * scale 1, bit for bit, without the intermediate buffers. 1 <= n_instances,
+ * n_instances * D <= ZDO_MAX_REPLICAS (else ZDO_EINVAL). Other arguments and
+ * rules as sharded_adam_step. */
+int sharded_adam_step_instances(const zdo_plan *plan, const uint16_t *const *grads, int32_t n_instances,
+                                int32_t grad_coords, float scale, float *master, float *exp_avg,
+                                float *exp_avg_sq, uint16_t *param_out, int32_t param_coords,
+                                const zdo_adam *hp, float *main_grad_out, void *stream);
+
 /* bf16(master) into the owned parameter elements of param_out (page 1, §4.3:
  * the updated master shard copied back into the buffer's owned range).
  * master: fp32, L elements; param_out: bf16, N (ZDO_WORLD) or L (ZDO_LOCAL)

@@ -646,58 +646,113 @@ def test_bucket_ranges(gpu, name):
 
 # ---- several distributed-optimizer instances ----------------------------------------------
 
-@pytest.mark.parametrize("D,n_inst", [(4, 2), (8, 4), (2, 3), (16, 2)])
-def test_two_level_instances(gpu, D, n_inst):
+def _own_mask(lay, r, Ln):
+    own = np.zeros(Ln, bool)
+    for pc in OL.rank_pieces(lay, r):
+        own[pc.shard_offset:pc.shard_offset + pc.gbuf_world.size] = True
+    return own
+
+
+@pytest.mark.parametrize("D,n_inst,coords", [(4, 2, "world"), (8, 4, "local"), (2, 3, "world"), (16, 2, "local"),
+                                             (3, 5, "world"), (1, 4, "local"), (5, 1, "world"), (32, 2, "local")])
+def test_two_level_instances(gpu, D, n_inst, coords):
     """Page 1, §5: the reduce-scatter runs within each instance of D ranks and
-    an all-reduce across the n_inst instances follows. On the GPU: one
-    reduce_scatter_local per instance, then the step (and the reduced gradient
-    alone) on the instances' results with scale 1; against the oracle's same
-    composition, bit for bit."""
+    an all-reduce across the n_inst instances follows. The oracle composes one
+    reduce-scatter per instance and the step on the instance results (scale
+    1). On the GPU the same composition through the existing calls, and the
+    one-pass sharded_adam_step_instances, both bit for bit against it."""
     rng = np.random.default_rng(100 * D + n_inst)
     sizes, bucket = [5000, 13, 20000, 1, 4097, 2200], 9000
     lay = OL.build_layout(sizes, bucket, D)
     N = lay.buffer_numel
     reps_h = [[bf16_host(rng, N) for _ in range(D)] for _ in range(n_inst)]
-    reps_d = [[to_dev(x) for x in inst] for inst in reps_h]
-    scale = 1.0 / (D * n_inst)
+    scale = float(np.float32(1.0 / (D * n_inst)))
     hp = W.get("tiny").hp
+    gc = gpu.WORLD if coords == "world" else gpu.LOCAL
     for r in sorted({0, D - 1, int(rng.integers(D))}):
         plan = gpu.build_range_map(sizes, bucket, D, r)
         Ln = plan.shard_numel
-        rs_d, rs_h = [], []
+        src_h = [[x if gc == gpu.WORLD else OS.local_slices(lay, r, x) for x in inst] for inst in reps_h]
+        src_d = [[to_dev(x) for x in inst] for inst in src_h]
+        # oracle: reduce-scatter within each instance, then the step on the results
+        rs_h = []
         for i in range(n_inst):
-            out = torch.zeros(Ln, dtype=torch.int16, device=DEV)
-            gpu.reduce_scatter_local(plan, reps_d[i], gpu.WORLD, scale, out, gpu.LOCAL)
-            rs_d.append(out)
             want = np.zeros(Ln, np.uint16)
-            OS.reduce_scatter(lay, r, reps_h[i], OS.WORLD, scale, want, OS.LOCAL)
+            OS.reduce_scatter(lay, r, src_h[i], gc, scale, want, OS.LOCAL)
             rs_h.append(want)
-            assert_bf16(host_u16(out), want, f"instance {i} rs")
-        red = torch.zeros(Ln, dtype=torch.int16, device=DEV)
-        gpu.reduce_scatter_local(plan, rs_d, gpu.LOCAL, 1.0, red, gpu.LOCAL)
         want_red = np.zeros(Ln, np.uint16)
         OS.reduce_scatter(lay, r, rs_h, OS.LOCAL, 1.0, want_red, OS.LOCAL)
-        assert_bf16(host_u16(red), want_red, "all-reduce across instances")
-        # the step on the instances' results, against the oracle's step on them
         state_h = [(rng.standard_normal(Ln) * 0.02).astype(np.float32),
                    (rng.standard_normal(Ln) * 1e-3).astype(np.float32),
                    ((rng.standard_normal(Ln) * 1e-3) ** 2).astype(np.float32)]
-        master, m, v = (to_dev(x) for x in state_h)
-        par = torch.full((max(N, 8),), SENTINEL, dtype=torch.int16, device=DEV)
-        mg = torch.full((max(Ln, 8),), -7.0, dtype=torch.float32, device=DEV)
-        gpu.sharded_adam_step(plan, rs_d, gpu.LOCAL, 1.0, master, m, v, par, gpu.WORLD, main_grad_out=mg,
-                              **hp_kwargs(hp, 3))
         want = [x.copy() for x in state_h]
         want_par = np.full(max(N, 8), SENTINEL, np.uint16)
         want_mg = np.full(max(Ln, 8), -7.0, np.float32)
         OS.rank_step(lay, r, rs_h, OS.LOCAL, 1.0, *want, ON.hp_array(hp, 3), want_par, OS.WORLD, want_mg[:Ln])
-        for got, w, name in zip((master, m, v), want, ("master", "exp_avg", "exp_avg_sq")):
-            assert_f32(host_f32(got), w, f"{name} r={r}")
-        assert_bf16(host_u16(par), want_par, f"params r={r}")
-        assert_f32(host_f32(mg), want_mg, f"main grad r={r}")
-        # on the owned elements the main grad is the widened all-reduced gradient
-        own = np.zeros(Ln, bool)
-        for pc in OL.rank_pieces(lay, r):
-            own[pc.shard_offset:pc.shard_offset + pc.gbuf_world.size] = True
-        assert_f32(host_f32(mg)[:Ln][own], ON.widen(want_red)[own], "main grad = widen(all-reduce)")
+        own = _own_mask(lay, r, Ln)
+        assert np.array_equal(want_mg[:Ln][own], ON.widen(want_red)[own])
+
+        # GPU, composed: one reduce_scatter_local per instance, then the step
+        rs_d = []
+        for i in range(n_inst):
+            out = torch.zeros(Ln, dtype=torch.int16, device=DEV)
+            gpu.reduce_scatter_local(plan, src_d[i], gc, scale, out, gpu.LOCAL)
+            assert_bf16(host_u16(out), rs_h[i], f"instance {i} rs r={r}")
+            rs_d.append(out)
+        red = torch.zeros(Ln, dtype=torch.int16, device=DEV)
+        gpu.reduce_scatter_local(plan, rs_d, gpu.LOCAL, 1.0, red, gpu.LOCAL)
+        assert_bf16(host_u16(red), want_red, f"all-reduce across instances r={r}")
+
+        def run(fused: bool):
+            master, m, v = (to_dev(x) for x in state_h)
+            par = torch.full((max(N, 8),), SENTINEL, dtype=torch.int16, device=DEV)
+            mg = torch.full((max(Ln, 8),), -7.0, dtype=torch.float32, device=DEV)
+            if fused:
+                gpu.sharded_adam_step_instances(plan, src_d, gc, scale, master, m, v, par, gpu.WORLD,
+                                                main_grad_out=mg, **hp_kwargs(hp, 3))
+            else:
+                gpu.sharded_adam_step(plan, rs_d, gpu.LOCAL, 1.0, master, m, v, par, gpu.WORLD, main_grad_out=mg,
+                                      **hp_kwargs(hp, 3))
+            what = f"{'one pass' if fused else 'composed'} r={r}"
+            for got, w, name in zip((master, m, v), want, ("master", "exp_avg", "exp_avg_sq")):
+                assert_f32(host_f32(got), w, f"{name} {what}")
+            assert_bf16(host_u16(par), want_par, f"params {what}")
+            assert_f32(host_f32(mg), want_mg, f"main grad {what}")
+
+        run(False)
+        run(True)
     free()
+
+
+def test_instances_one_instance_is_the_plain_step(gpu):
+    """n_instances = 1 is sharded_adam_step on the D contributions."""
+    rng = np.random.default_rng(77)
+    sizes, bucket, D, r = [3000, 7, 9000, 515], 5000, 8, 3
+    plan = gpu.build_range_map(sizes, bucket, D, r)
+    reps = [to_dev(bf16_host(rng, plan.buffer_numel)) for _ in range(D)]
+    Ln = plan.shard_numel
+    st0 = [(rng.standard_normal(Ln) * 0.02).astype(np.float32), np.zeros(Ln, np.float32), np.zeros(Ln, np.float32)]
+    hp = hp_kwargs(W.get("tiny").hp, 1)
+    outs = []
+    for fused in (False, True):
+        st = [to_dev(x) for x in st0]
+        par = torch.full((plan.buffer_numel,), SENTINEL, dtype=torch.int16, device=DEV)
+        if fused:
+            gpu.sharded_adam_step_instances(plan, [reps], gpu.WORLD, 0.125, *st, par, gpu.WORLD, **hp)
+        else:
+            gpu.sharded_adam_step(plan, reps, gpu.WORLD, 0.125, *st, par, gpu.WORLD, **hp)
+        outs.append([host_f32(x) for x in st] + [host_u16(par)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    # argument checks
+    st = [to_dev(x) for x in st0]
+    with pytest.raises(gpu.ZdoError) as e:
+        gpu.sharded_adam_step_instances(plan, [], gpu.WORLD, 1.0, *st, None, gpu.WORLD, **hp)
+    assert e.value.code == gpu.EINVAL
+    with pytest.raises(gpu.ZdoError) as e:
+        gpu.sharded_adam_step_instances(plan, [reps] * 9, gpu.WORLD, 1.0, *st, None, gpu.WORLD, **hp)  # 72 > 64
+    assert e.value.code == gpu.EINVAL
+    with pytest.raises(ValueError):
+        gpu.sharded_adam_step_instances(plan, [reps, reps[:7]], gpu.WORLD, 1.0, *st, None, gpu.WORLD, **hp)
+    free()
+

@@ -68,7 +68,7 @@ EXPORTS = ("build_range_map", "zdo_plan_destroy", "zdo_plan_buffer_numel", "zdo_
            "zdo_plan_pieces", "reduce_scatter_local", "force_all_reduce", "sharded_adam_step",
            "writeback_params", "reduce_scatter_local_buckets", "sharded_adam_step_buckets",
            "zdo_plan_norm_workspace_bytes", "grad_norm_sq", "clip_coefficient", "sharded_adam_step_clipped",
-           "zdo_device_copy", "zdo_last_error")
+           "sharded_adam_step_instances", "zdo_device_copy", "zdo_last_error")
 
 _lib = None
 
@@ -107,6 +107,8 @@ def require_library() -> ctypes.CDLL:
     L.clip_coefficient.argtypes = [vp, i32, f32, vp, vp, vp]
     L.sharded_adam_step_clipped.argtypes = [vp, vp, i32, i32, f32, vp, vp, vp, vp, i32, ctypes.POINTER(Adam),
                                             vp, vp, vp]
+    L.sharded_adam_step_instances.argtypes = [vp, vp, i32, i32, f32, vp, vp, vp, vp, i32, ctypes.POINTER(Adam), vp,
+                                              vp]
     L.zdo_device_copy.argtypes = [vp, vp, i64, vp]
     L.zdo_last_error.argtypes = []
     L.zdo_last_error.restype = ctypes.c_char_p
@@ -287,6 +289,30 @@ def sharded_adam_step_clipped(plan: Plan, grads, grad_coords: int, scale: float,
     _check(require_library().sharded_adam_step_clipped(plan.handle, g, len(grads), grad_coords, scale, m, a, s, p,
                                                        param_coords, ctypes.byref(hp), c, mg,
                                                        _stream(stream, master.device)))
+
+
+def sharded_adam_step_instances(plan: Plan, instances, grad_coords: int, scale: float, master, exp_avg,
+                                exp_avg_sq, param_out=None, param_coords: int = WORLD, *, lr: float, beta1: float,
+                                beta2: float, eps: float, weight_decay: float, step: int, main_grad_out=None,
+                                stream=None) -> None:
+    """The step for several optimizer instances in one pass: instances is a
+    sequence of n_instances sequences of D gradient tensors each."""
+    flat = []
+    for i, inst in enumerate(instances):
+        if len(inst) != plan.dp_size:
+            raise ValueError(f"instance {i} has {len(inst)} gradients, the plan's D is {plan.dp_size}")
+        flat.extend(inst)
+    L = plan.shard_numel
+    g = _ptr_list(flat, "grads", plan.extent(grad_coords))
+    m = _dev_ptr(master, "master", "f32", L)
+    a = _dev_ptr(exp_avg, "exp_avg", "f32", L)
+    s = _dev_ptr(exp_avg_sq, "exp_avg_sq", "f32", L)
+    p = None if param_out is None else _dev_ptr(param_out, "param_out", "bf16", plan.extent(param_coords))
+    mg = None if main_grad_out is None else _dev_ptr(main_grad_out, "main_grad_out", "f32", L)
+    hp = adam_hparams(lr, beta1, beta2, eps, weight_decay, step)
+    _check(require_library().sharded_adam_step_instances(plan.handle, g, len(instances), grad_coords, scale, m, a, s,
+                                                         p, param_coords, ctypes.byref(hp), mg,
+                                                         _stream(stream, master.device)))
 
 
 def grad_norm_sq(plan: Plan, replicas, replica_coords: int, scale: float, workspace, norm_sq_out,

@@ -300,8 +300,10 @@ int force_all_reduce(const zdo_plan *plan, const uint16_t *const *replicas, int3
     return launch_result(launch_reduce(a, plan->lds_per_cu, static_cast<hipStream_t>(stream)), fn);
 }
 
+// n_instances groups of n_grads / n_instances contributions (1 for the plain
+// step).
 static int adam_step(const char *fn, const zdo_plan *plan, int32_t b0, int32_t b1, const uint16_t *const *grads,
-                     int32_t n_grads, int32_t grad_coords, float scale, float *master, float *exp_avg,
+                     int32_t n_grads, int32_t n_instances, int32_t grad_coords, float scale, float *master, float *exp_avg,
                      float *exp_avg_sq, uint16_t *param_out, int32_t param_coords, const zdo_adam *hp,
                      const float *coeff, float *main_grad_out, void *stream) {
     if (int rc = check_plan(plan, fn))
@@ -372,6 +374,8 @@ static int adam_step(const char *fn, const zdo_plan *plan, int32_t b0, int32_t b
     bucket_tiles(plan->param_segs, plan->param_seg_bucket.data(), plan->param_tiles, b0, b1, first, count);
     a.walk = {plan->d_param_segs, plan->d_param_tile_seg, count, 0, int64_t(plan->param_segs.size()), first};
     a.nrep = n_grads;
+    a.ninst = n_instances;
+    a.dinst = n_grads / n_instances;
     a.in_local = grad_coords == ZDO_LOCAL;
     a.param_local = param_coords == ZDO_LOCAL;
     a.scale = scale;
@@ -396,7 +400,7 @@ static int adam_step(const char *fn, const zdo_plan *plan, int32_t b0, int32_t b
 int sharded_adam_step(const zdo_plan *plan, const uint16_t *const *grads, int32_t n_grads, int32_t grad_coords,
                       float scale, float *master, float *exp_avg, float *exp_avg_sq, uint16_t *param_out,
                       int32_t param_coords, const zdo_adam *hp, float *main_grad_out, void *stream) {
-    return adam_step("sharded_adam_step", plan, 0, -1, grads, n_grads, grad_coords, scale, master, exp_avg,
+    return adam_step("sharded_adam_step", plan, 0, -1, grads, n_grads, 1, grad_coords, scale, master, exp_avg,
                      exp_avg_sq, param_out, param_coords, hp, nullptr, main_grad_out, stream);
 }
 
@@ -406,7 +410,7 @@ int sharded_adam_step_buckets(const zdo_plan *plan, int32_t bucket_begin, int32_
                               int32_t param_coords, const zdo_adam *hp, float *main_grad_out, void *stream) {
     if (bucket_end < 0)
         return fail(ZDO_EINVAL, "sharded_adam_step_buckets: bucket_end < 0");
-    return adam_step("sharded_adam_step_buckets", plan, bucket_begin, bucket_end, grads, n_grads, grad_coords, scale,
+    return adam_step("sharded_adam_step_buckets", plan, bucket_begin, bucket_end, grads, n_grads, 1, grad_coords, scale,
                      master, exp_avg, exp_avg_sq, param_out, param_coords, hp, nullptr, main_grad_out, stream);
 }
 
@@ -416,8 +420,22 @@ int sharded_adam_step_clipped(const zdo_plan *plan, const uint16_t *const *grads
                               const float *grad_coeff, float *main_grad_out, void *stream) {
     if (!grad_coeff)
         return fail(ZDO_EINVAL, "sharded_adam_step_clipped: grad_coeff is NULL");
-    return adam_step("sharded_adam_step_clipped", plan, 0, -1, grads, n_grads, grad_coords, scale, master, exp_avg,
+    return adam_step("sharded_adam_step_clipped", plan, 0, -1, grads, n_grads, 1, grad_coords, scale, master, exp_avg,
                      exp_avg_sq, param_out, param_coords, hp, grad_coeff, main_grad_out, stream);
+}
+
+int sharded_adam_step_instances(const zdo_plan *plan, const uint16_t *const *grads, int32_t n_instances,
+                                int32_t grad_coords, float scale, float *master, float *exp_avg, float *exp_avg_sq,
+                                uint16_t *param_out, int32_t param_coords, const zdo_adam *hp, float *main_grad_out,
+                                void *stream) {
+    const char *fn = "sharded_adam_step_instances";
+    if (int rc = check_plan(plan, fn))
+        return rc;
+    if (n_instances < 1 || int64_t(n_instances) * plan->dp_size > ZDO_MAX_REPLICAS)
+        return fail(ZDO_EINVAL, std::string(fn) + ": n_instances must be >= 1 with n_instances * D <= " +
+                                    std::to_string(ZDO_MAX_REPLICAS));
+    return adam_step(fn, plan, 0, -1, grads, n_instances * plan->dp_size, n_instances, grad_coords, scale, master,
+                     exp_avg, exp_avg_sq, param_out, param_coords, hp, nullptr, main_grad_out, stream);
 }
 
 int64_t zdo_plan_norm_workspace_bytes(const zdo_plan *p) {

@@ -38,6 +38,11 @@ struct StepArgs {
     Walk walk;
     const uint16_t *rep[ZDO_MAX_REPLICAS];
     int32_t nrep;
+    // Several optimizer instances: rep holds ninst groups of dinst
+    // contributions (nrep = ninst * dinst), reduced within each group first.
+    // ninst = 1, dinst = nrep for the plain step.
+    int32_t ninst;
+    int32_t dinst;
     int32_t in_local;
     int32_t param_local;
     float scale;

@@ -143,6 +143,41 @@ __device__ __forceinline__ float reduce_one(const uint16_t *const *rep, int nrep
     return acc;
 }
 
+// Several optimizer instances: instance i's contributions rep[i*d .. i*d+d)
+// reduced as above and rounded to bf16 (what the instance's reduce-scatter
+// leaves in its grad buffer), then those bf16 results added in fp32 in
+// instance order (the all-reduce across instances).
+template <int D>
+__device__ __forceinline__ void reduce_chunk_instances(const uint16_t *const *rep, int d, int ninst, int64_t gi,
+                                                       float scale, float acc[8]) {
+    float part[8];
+    reduce_chunk<D>(rep, d, gi, scale, part);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t r = to_bf16x2(part[2 * k], part[2 * k + 1]);
+        acc[2 * k] = lo_f32(r);
+        acc[2 * k + 1] = hi_f32(r);
+    }
+    for (int i = 1; i < ninst; ++i) {
+        reduce_chunk<D>(rep + i * d, d, gi, scale, part);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t r = to_bf16x2(part[2 * k], part[2 * k + 1]);
+            acc[2 * k] = acc[2 * k] + lo_f32(r);
+            acc[2 * k + 1] = acc[2 * k + 1] + hi_f32(r);
+        }
+    }
+}
+
+template <int D>
+__device__ __forceinline__ float reduce_one_instances(const uint16_t *const *rep, int d, int ninst, int64_t i,
+                                                      float scale) {
+    float acc = lo_f32(to_bf16x2(reduce_one<D>(rep, d, i, scale), 0.0f));
+    for (int k = 1; k < ninst; ++k)
+        acc = acc + lo_f32(to_bf16x2(reduce_one<D>(rep + k * d, d, i, scale), 0.0f));
+    return acc;
+}
+
 // ---- Adam --------------------------------------------------------------------------------------
 __device__ __forceinline__ void adam(const AdamConst &c, float g, float &p, float &m, float &v) {
     const float m1 = c.b1 * m;
@@ -192,7 +227,9 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceArgs a) {
     }
 }
 
-template <int D>
+// kInst: a.rep holds a.ninst instances of D (or, for D = 0, a.dinst)
+// contributions each; otherwise a.nrep contributions of one instance.
+template <int D, bool kInst>
 __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a) {
     // Global-norm clipping: the main grad is multiplied by the coefficient; a
     // NaN coefficient (found-inf) leaves everything unchanged.
@@ -213,7 +250,10 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a) {
         const int64_t k0 = c.k0;
         if (c.lo == 0 && c.hi == kChunk) {
             float acc[8];
-            reduce_chunk<D>(a.rep, a.nrep, gi, a.scale, acc);
+            if constexpr (kInst)
+                reduce_chunk_instances<D>(a.rep, a.dinst, a.ninst, gi, a.scale, acc);
+            else
+                reduce_chunk<D>(a.rep, a.nrep, gi, a.scale, acc);
             float g[8], p[8], m[8], v[8];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -258,7 +298,8 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a) {
             }
         } else {
             for (int e = c.lo; e < c.hi; ++e) {
-                const float acc = reduce_one<D>(a.rep, a.nrep, gi + e, a.scale);
+                const float acc = kInst ? reduce_one_instances<D>(a.rep, a.dinst, a.ninst, gi + e, a.scale)
+                                        : reduce_one<D>(a.rep, a.nrep, gi + e, a.scale);
                 float g = lo_f32(to_bf16x2(acc, 0.0f));
                 if (clip)
                     g = g * cf;
@@ -453,14 +494,27 @@ hipError_t launch_step(const StepArgs &a, int lds_per_cu, hipStream_t stream) {
         return hipSuccess;
     const dim3 grid(grid_for(a.walk.ntiles)), block(kBlock);
     const unsigned lds = lds_reserve(lds_per_cu);
+    // One contribution per instance is the plain sum over the instances: the
+    // inner rounding of a single bf16 term changes nothing.
+    if (a.ninst > 1 && a.dinst > 1) {
+        switch (a.dinst) {
+        case 2: hipLaunchKernelGGL((step_kernel<2, true>), grid, block, lds, stream, a); break;
+        case 4: hipLaunchKernelGGL((step_kernel<4, true>), grid, block, lds, stream, a); break;
+        case 8: hipLaunchKernelGGL((step_kernel<8, true>), grid, block, lds, stream, a); break;
+        case 16: hipLaunchKernelGGL((step_kernel<16, true>), grid, block, lds, stream, a); break;
+        case 32: hipLaunchKernelGGL((step_kernel<32, true>), grid, block, lds, stream, a); break;
+        default: hipLaunchKernelGGL((step_kernel<0, true>), grid, block, lds, stream, a); break;
+        }
+        return hipGetLastError();
+    }
     switch (a.nrep) {
-    case 1: hipLaunchKernelGGL(step_kernel<1>, grid, block, lds, stream, a); break;
-    case 2: hipLaunchKernelGGL(step_kernel<2>, grid, block, lds, stream, a); break;
-    case 4: hipLaunchKernelGGL(step_kernel<4>, grid, block, lds, stream, a); break;
-    case 8: hipLaunchKernelGGL(step_kernel<8>, grid, block, lds, stream, a); break;
-    case 16: hipLaunchKernelGGL(step_kernel<16>, grid, block, lds, stream, a); break;
-    case 32: hipLaunchKernelGGL(step_kernel<32>, grid, block, lds, stream, a); break;
-    default: hipLaunchKernelGGL(step_kernel<0>, grid, block, lds, stream, a); break;
+    case 1: hipLaunchKernelGGL((step_kernel<1, false>), grid, block, lds, stream, a); break;
+    case 2: hipLaunchKernelGGL((step_kernel<2, false>), grid, block, lds, stream, a); break;
+    case 4: hipLaunchKernelGGL((step_kernel<4, false>), grid, block, lds, stream, a); break;
+    case 8: hipLaunchKernelGGL((step_kernel<8, false>), grid, block, lds, stream, a); break;
+    case 16: hipLaunchKernelGGL((step_kernel<16, false>), grid, block, lds, stream, a); break;
+    case 32: hipLaunchKernelGGL((step_kernel<32, false>), grid, block, lds, stream, a); break;
+    default: hipLaunchKernelGGL((step_kernel<0, false>), grid, block, lds, stream, a); break;
     }
     return hipGetLastError();
 }

@@ -97,12 +97,12 @@ def main() -> int:
     N, Ln, E = plan.buffer_numel, plan.shard_numel, plan.owned_numel
     coords = zdo.WORLD if w.grad_mode == "world" else zdo.LOCAL
     n_rep = N if coords == zdo.WORLD else Ln
-    stride = (n_rep + 7) // 8 * 8
+    stride = (n_rep + 63) // 64 * 64      # 128-byte-aligned replica buffers
     log(f"workload {w.name}: N={N} D={D} rank={rank} E={E} L={Ln} grads={w.grad_mode}")
 
     # inputs, resident in HBM before the timed region: the D replicas in one
-    # allocation, then the three state arrays in another, each buffer
-    # `stagger` bytes further from the previous one than its size requires
+    # allocation, then the three state arrays in another, each buffer starting
+    # on a 128-byte line (plus `stagger` bytes further from the previous one)
     if args.stagger % 16:
         raise SystemExit("--stagger must be a multiple of 16")
     t0 = time.perf_counter()
@@ -114,7 +114,7 @@ def main() -> int:
         W.normal_bf16(n_rep, w.grad_sigma, W.seed(w.cfg, 0, "grad", j), out=s,
                       probe_fraction=w.probe_fraction, probe_seed=W.seed(w.cfg, 0, "probe", j))
         reps.append(s.view(torch.int16))
-    sstride = (Ln + 3) // 4 * 4 + gap4
+    sstride = (Ln + 31) // 32 * 32 + gap4
     state_buf = torch.empty(3 * sstride, dtype=torch.float32, device=dev)
     master, exp_avg, exp_avg_sq = (state_buf[i * sstride: i * sstride + Ln] for i in range(3))
     W.normal_f32(Ln, w.master_sigma, W.seed(w.cfg, 0, "master"), out=master)
@@ -353,7 +353,7 @@ def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> d
     n_inst = 2
     Ln = plan.shard_numel
     n_rep = plan.extent(coords)
-    stride = (n_rep + 7) // 8 * 8
+    stride = (n_rep + 63) // 64 * 64
     need = 2 * D * stride + 2 * n_inst * Ln + 12 * Ln + 2 * n_rep + (1 << 30)
     if torch.cuda.mem_get_info(dev)[0] < need:
         out["two_level_instances"] = {"skipped": "not enough free device memory for a second instance"}

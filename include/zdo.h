@@ -119,8 +119,10 @@ typedef struct {
  * tail to a multiple of dp_size; and builds rank `rank`'s range map (page 1,
  * §2, §3, §4.1, §5). The rank's fp32 shard places each bucket's local view at
  * the first slot >= the previous view's end that is congruent to the range's
- * WORLD start modulo 8, so every LOCAL index is congruent to its WORLD index
- * modulo 8 (gap slots, < 8 per bucket, and padding slots are never touched).
+ * WORLD start modulo 64, so every LOCAL index is congruent to its WORLD index
+ * modulo 64 (gap slots, < 64 per bucket, and padding slots are never
+ * touched). With buffers aligned to 128 bytes, every stream then crosses
+ * cache lines at the same elements, which the kernels' tiles follow.
  * If a HIP device is present, the plan's segment table is uploaded to the
  * current device (the plan's device); otherwise the plan is host-only and
  * the launch calls fail with ZDO_EHIP. *out receives the plan, owned by the

@@ -36,7 +36,7 @@ from __future__ import annotations
 
 from dataclasses import dataclass
 
-SHARD_PHASE = 8  # elements: 16 bytes of bf16
+SHARD_PHASE = 64  # elements: one 128-byte line of bf16
 
 
 @dataclass(frozen=True)

@@ -4,11 +4,13 @@
 //
 // The step is a pure stream over the rank's elements: (2D + 26) bytes per
 // element against a few dozen VALU operations, so it is bound by HBM
-// bandwidth, not by the matrix cores. The layout makes every stream
-// 16-byte-phase-aligned together (a LOCAL index is congruent to its WORLD
-// index modulo 8). A workgroup is a single wave and takes a tile of 512
-// consecutive elements of one segment: 1 KiB of every bf16 stream and 2 KiB
-// of every fp32 stream, contiguously. In the reduce, norm and write-back
+// bandwidth, not by the matrix cores. A LOCAL index is congruent to its
+// WORLD index modulo 64, and a segment's tiles start at a multiple of 64
+// WORLD elements, so with 128-byte-aligned buffers every stream crosses cache
+// lines at tile boundaries only (no line is fetched by two workgroups). A
+// workgroup is a single wave and takes a tile of 512 consecutive elements of
+// one segment: 1 KiB of every bf16 stream and 2 KiB of every fp32 stream,
+// contiguously. In the reduce, norm and write-back
 // kernels lane l takes the 8-element chunk [8l, 8l + 8) of the tile (one
 // 16-byte load per bf16 stream); the step takes two quads per lane (see
 // there). Chunks or quads cut by a segment's ends take a per-element path.
@@ -68,7 +70,8 @@ struct ChunkPos {
     int lo, hi;     // the chunk's slots [lo, hi) that belong to the segment
 };
 
-// The chunk this thread takes in `tile`; false if the tile ends before it.
+// The chunk this thread takes in `tile`; false if it holds no element of the
+// segment.
 __device__ __forceinline__ bool chunk_of(const Walk &wk, int64_t tile, ChunkPos &c) {
     int64_t wbeg, lbeg, len, tile0;
     if (wk.segs) {
@@ -83,13 +86,12 @@ __device__ __forceinline__ bool chunk_of(const Walk &wk, int64_t tile, ChunkPos 
         len = wk.flat_numel;
         tile0 = 0;
     }
-    const int64_t q0 = wbeg / kChunk;
-    const int64_t w0 = (q0 + (tile - tile0) * kBlock + threadIdx.x) * kChunk;
+    const int64_t w0 = tile_origin(wbeg) + (tile - tile0) * kTileElems + int64_t(threadIdx.x) * kChunk;
     const int64_t wend = wbeg + len;
-    if (w0 >= wend)
+    if (w0 >= wend || w0 + kChunk <= wbeg)
         return false;
     c.w0 = w0;
-    c.k0 = lbeg - (wbeg - q0 * kChunk) + (w0 - q0 * kChunk);
+    c.k0 = lbeg + (w0 - wbeg);
     c.lo = w0 < wbeg ? int(wbeg - w0) : 0;
     c.hi = w0 + kChunk > wend ? int(wend - w0) : kChunk;
     return true;
@@ -243,7 +245,7 @@ __device__ __forceinline__ void quads_of(const Walk &wk, int64_t tile, Quad q[2]
         len = wk.flat_numel;
         tile0 = 0;
     }
-    const int64_t tw = (wbeg / kChunk) * kChunk + (tile - tile0) * kTileElems;
+    const int64_t tw = tile_origin(wbeg) + (tile - tile0) * kTileElems;
     const int64_t wend = wbeg + len;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {

@@ -83,11 +83,11 @@ int build_plan(const int64_t *param_numel, int32_t n_params, int64_t bucket_nume
 
     // The rank's shard: per bucket, the local view starts at the first slot
     // at or after the previous view's end that has the WORLD start's phase
-    // modulo 8.
+    // modulo kAnchor (64).
     int64_t end = 0;
     for (auto &b : p.buckets) {
         const int64_t rstart = b.offset + int64_t(rank) * b.shard_numel;
-        b.shard_base = end + floor_mod(rstart - end, kChunk);
+        b.shard_base = end + floor_mod(rstart - end, kAnchor);
         end = b.shard_base + b.shard_numel;
     }
     p.shard_numel = end;

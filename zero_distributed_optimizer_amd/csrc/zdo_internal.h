@@ -21,18 +21,20 @@ constexpr int kTileElems = kChunk * kBlock;
 // One contiguous run of the rank's elements, as the kernels walk it.
 struct Seg {
     int64_t wbeg;   // WORLD index of the first element
-    int64_t lbeg;   // LOCAL (shard) index of the first element; lbeg == wbeg (mod 8)
+    int64_t lbeg;   // LOCAL (shard) index of the first element; lbeg == wbeg (mod kAnchor)
     int64_t len;    // elements, >= 1
     int64_t tile0;  // index of the segment's first tile in the launch's tile space
 };
 
-// Tiles a segment needs: its 8-element chunks (aligned to the WORLD index,
-// so a partial chunk at each end) in groups of kBlock.
-inline int64_t seg_chunks(int64_t wbeg, int64_t len) {
-    return (wbeg + len + kChunk - 1) / kChunk - wbeg / kChunk;
-}
+// A segment's tiles start at its first WORLD index rounded down to a
+// multiple of kAnchor (64 elements: one 128-byte cache line of bf16), so
+// that, at a given alignment of the buffers, a tile's runs never share a
+// cache line with the next tile's.
+constexpr int64_t kAnchor = 64;
+constexpr int64_t tile_origin(int64_t wbeg) { return wbeg / kAnchor * kAnchor; }
+// Tiles a segment needs: kTileElems-element steps from its origin to its end.
 inline int64_t seg_tiles(int64_t wbeg, int64_t len) {
-    return (seg_chunks(wbeg, len) + kBlock - 1) / kBlock;
+    return (wbeg + len - tile_origin(wbeg) + kTileElems - 1) / kTileElems;
 }
 
 void set_error(const std::string &msg);

@@ -565,19 +565,30 @@ unsigned grid_for(int64_t ntiles) {
     return unsigned(ntiles < kMaxGrid ? ntiles : kMaxGrid);
 }
 
-// HBM serves the step's mix of read and write streams at a higher rate when
-// fewer waves share a compute unit (measured on the 42 GB Llama-3-8B-shaped
-// step: 5.32 TB/s uncapped, 5.69 TB/s at 10 waves per compute unit, 5.66 at
-// 8, 5.55 at 14): the launch reserves LDS it never uses so that at most
-// ZDO_WAVES_PER_CU waves fit on one compute unit.
+// HBM serves a long stream of many read and write streams at a higher rate
+// when fewer waves share a compute unit (measured on the 42 GB
+// Llama-3-8B-shaped step: 5.32 TB/s uncapped, 5.69 TB/s at 10 waves per
+// compute unit, 5.66 at 8, 5.55 at 14), while a short launch, a few dozen
+// rounds of workgroups over the chip, finishes sooner with more waves in
+// flight (GPT-2-shaped step, 30k tiles: 106 us at 10 waves per compute unit,
+// 102 us at 16; its clipped step 92 us at 10, 78 us at 16). The launch
+// reserves LDS it never uses so that at most ZDO_WAVES_PER_CU waves, or
+// ZDO_WAVES_PER_CU_SHORT for launches of fewer than kShortLaunchTiles tiles,
+// fit on one compute unit.
 #ifndef ZDO_WAVES_PER_CU
 #define ZDO_WAVES_PER_CU 10
 #endif
-unsigned lds_reserve(int lds_per_cu) {
-    if (ZDO_WAVES_PER_CU <= 0 || lds_per_cu <= 0)
+#ifndef ZDO_WAVES_PER_CU_SHORT
+#define ZDO_WAVES_PER_CU_SHORT 16
+#endif
+constexpr int64_t kShortLaunchTiles = int64_t(1) << 17;
+
+unsigned lds_reserve(int lds_per_cu, int64_t ntiles) {
+    const int waves = ntiles < kShortLaunchTiles ? ZDO_WAVES_PER_CU_SHORT : ZDO_WAVES_PER_CU;
+    if (waves <= 0 || lds_per_cu <= 0)
         return 0;
     const int waves_per_group = kBlock / 64;
-    int groups = ZDO_WAVES_PER_CU / waves_per_group;
+    int groups = waves / waves_per_group;
     if (groups < 4 / waves_per_group + (waves_per_group > 4))
         groups = 4 / waves_per_group + (waves_per_group > 4);
     return unsigned(lds_per_cu / groups) & ~127u;
@@ -589,7 +600,7 @@ hipError_t launch_reduce(const ReduceArgs &a, int lds_per_cu, hipStream_t stream
     if (a.walk.ntiles <= 0)
         return hipSuccess;
     const dim3 grid(grid_for(a.walk.ntiles)), block(kBlock);
-    const unsigned lds = lds_reserve(lds_per_cu);
+    const unsigned lds = lds_reserve(lds_per_cu, a.walk.ntiles);
     switch (a.nrep) {
     case 1: hipLaunchKernelGGL(reduce_kernel<1>, grid, block, lds, stream, a); break;
     case 2: hipLaunchKernelGGL(reduce_kernel<2>, grid, block, lds, stream, a); break;
@@ -606,7 +617,7 @@ hipError_t launch_step(const StepArgs &a, int lds_per_cu, hipStream_t stream) {
     if (a.walk.ntiles <= 0)
         return hipSuccess;
     const dim3 grid(grid_for(a.walk.ntiles)), block(kBlock);
-    const unsigned lds = lds_reserve(lds_per_cu);
+    const unsigned lds = lds_reserve(lds_per_cu, a.walk.ntiles);
     // One contribution per instance is the plain sum over the instances: the
     // inner rounding of a single bf16 term changes nothing.
     if (a.ninst > 1 && a.dinst > 1) {
@@ -635,15 +646,15 @@ hipError_t launch_step(const StepArgs &a, int lds_per_cu, hipStream_t stream) {
 hipError_t launch_writeback(const WritebackArgs &a, int lds_per_cu, hipStream_t stream) {
     if (a.walk.ntiles <= 0)
         return hipSuccess;
-    hipLaunchKernelGGL(writeback_kernel, dim3(grid_for(a.walk.ntiles)), dim3(kBlock), lds_reserve(lds_per_cu), stream,
-                       a);
+    hipLaunchKernelGGL(writeback_kernel, dim3(grid_for(a.walk.ntiles)), dim3(kBlock),
+                       lds_reserve(lds_per_cu, a.walk.ntiles), stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_norm(const NormArgs &a, double *norm_sq, int lds_per_cu, hipStream_t stream) {
     if (a.walk.ntiles > 0) {
         const dim3 grid(grid_for(a.walk.ntiles)), block(kBlock);
-        const unsigned lds = lds_reserve(lds_per_cu);
+        const unsigned lds = lds_reserve(lds_per_cu, a.walk.ntiles);
         switch (a.nrep) {
         case 1: hipLaunchKernelGGL(norm_kernel<1>, grid, block, lds, stream, a); break;
         case 2: hipLaunchKernelGGL(norm_kernel<2>, grid, block, lds, stream, a); break;

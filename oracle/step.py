@@ -85,6 +85,17 @@ def all_reduce(grads, scale: float) -> np.ndarray:
     return N.reduce(list(grads), scale)
 
 
+def all_gather(layout: L.Layout, params, out: np.ndarray) -> None:
+    """Page 1, §4.4: after the step every bucket's parameter buffer is
+    all-gathered, so that every rank holds the whole updated parameters: rank
+    j's range of each bucket (padding included) is taken from params[j], the
+    buffer rank j wrote back into (WORLD coordinates)."""
+    for b in layout.buckets:
+        for j in range(layout.dp_size):
+            r = L.rank_range(b, layout.dp_size, j)
+            out[r.start:r.end] = params[j][r.start:r.end]
+
+
 def writeback(layout: L.Layout, rank: int, master: np.ndarray, param_out: np.ndarray,
               param_coords: int) -> None:
     """bf16(master) into the owned pieces of param_out (page 1, §4.3)."""

@@ -64,6 +64,8 @@ def _layout_pins():
         TS.test_split_parameter_is_updated_as_one,
         TS.test_all_reduce_restricted_is_reduce_scatter,
         TS.test_writeback_touches_owned_range_only,
+        lambda: TS.test_all_gather_closes_the_zero1_loop(0),
+        lambda: TS.test_all_gather_closes_the_zero1_loop(1),
     ]
 
 
@@ -189,6 +191,13 @@ PY_MUTANTS = {
     "piece's shard slot from gbuf_local only": ("step", [
         ("k0 = pc.shard_offset\n        k1 = k0 + pc.gbuf_world.size\n        g0, g1 = _span(grad_coords",
          "k0 = pc.gbuf_local.start\n        k1 = k0 + pc.gbuf_world.size\n        g0, g1 = _span(grad_coords")]),
+    "all-gather takes every range from the first rank's buffer": ("step", [
+        ("            out[r.start:r.end] = params[j][r.start:r.end]",
+         "            out[r.start:r.end] = params[0][r.start:r.end]")]),
+    "all-gather leaves the padding out": ("step", [
+        ("            r = L.rank_range(b, layout.dp_size, j)\n            out[r.start:r.end]",
+         "            r = L.rank_range(b, layout.dp_size, j)\n            r = L.Range(r.start, min(r.end, b.offset + b.numel))\n"
+         "            out[r.start:r.end]")]),
     "reduce-scatter over the parameter pieces only": ("step", [
         ("    for b, (world, base) in enumerate(L.rank_ranges(layout, rank)):",
          "    for b, (world, base) in enumerate([(pc.gbuf_world, pc.shard_offset)\n"

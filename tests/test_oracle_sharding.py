@@ -317,3 +317,40 @@ def test_two_level_reduction_of_instances():
     flat = S.all_reduce([x for inst in reps for x in inst], 0.125)
     two = [S.all_reduce(inst, 0.125) for inst in reps]
     assert (S.all_reduce(two, 1.0) != flat).any()
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_all_gather_closes_the_zero1_loop(seed):
+    """Page 1, §4.4: reduce-scatter of the grads, the sharded step, then the
+    all-gather of the parameters closes the ZeRO-1 loop: every rank writes
+    back into its own copy of the parameter buffer, and the all-gather of
+    those D buffers equals the unsharded step's parameters at every element
+    (padding keeps the buffer's prior contents), in a fresh buffer and in
+    place into any rank's buffer."""
+    rng = np.random.default_rng(500 + seed)
+    pr = random.Random(500 + seed)
+    sizes = [pr.randint(1, 400) for _ in range(pr.randint(1, 25))]
+    D = pr.choice([1, 2, 3, 4, 5, 8, 16])
+    lay = L.build_layout(sizes, pr.randint(1, 2000), D)
+    Nn = lay.buffer_numel
+    grads, master, m, v = make_inputs(lay, rng)
+    scale = pr.choice([1.0, 1.0 / D])
+    hp = N.hp_array(HP, pr.randint(1, 20))
+    before = bf16(master)
+    before[rng.random(Nn) < 0.1] = 0x7FBF          # prior contents, padding included
+    want = before.copy()
+    S.unsharded_step(lay, grads, scale, master.copy(), m.copy(), v.copy(), hp, want)
+    bufs = []
+    for r in range(D):
+        pb = before.copy()
+        S.rank_step(lay, r, grads, S.WORLD, scale, S.gather_shard(lay, r, master), S.gather_shard(lay, r, m),
+                    S.gather_shard(lay, r, v), hp, pb, S.WORLD)
+        bufs.append(pb)
+    if D > 1 and sum(1 for b in bufs if not np.array_equal(b, want)) < 2:
+        pytest.skip("layout where at most one rank owns elements")
+    out = np.full(Nn, 0x1234, np.uint16)
+    S.all_gather(lay, bufs, out)
+    assert np.array_equal(out, want)
+    k = pr.randrange(D)
+    S.all_gather(lay, bufs, bufs[k])
+    assert np.array_equal(bufs[k], want)

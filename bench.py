@@ -254,9 +254,10 @@ def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> d
     the rank's whole ranges (2D + 2 bytes per element of the ranges), the step
     bucket by bucket, the clipped path, two instances (composed from a
     reduce-scatter within each and the step on both results, and in one
-    pass) and, when the replicas are whole buffers, force_all_reduce over the
-    padded buffer (2D + 2 bytes per buffer element). HIP events around each
-    launch."""
+    pass), the parameter all-gather in place (4 bytes per element of the
+    other ranks' ranges) and, when the replicas are whole buffers,
+    force_all_reduce over the padded buffer (2D + 2 bytes per buffer
+    element). HIP events around each launch."""
     import workloads as W
 
     D = plan.dp_size
@@ -391,6 +392,32 @@ def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> d
             f"{t_st * 1e6:.1f} us ({bytes_all / t_all / 1e9:.0f} GB/s); one pass {t_one * 1e6:.1f} us "
             f"({bytes_one / t_one / 1e9:.0f} GB/s)")
         del extra, inst1, rs, st, par
+
+    # parameter all-gather, in place into this rank's buffer: the other ranks'
+    # ranges of every padded bucket copied from their buffers. Sources: the
+    # bench's whole-buffer replicas, else D uninitialised buffers of N if they
+    # fit (the copy's timing does not depend on the values)
+    N = plan.buffer_numel
+    ranges = int(sum(b["shard_numel"] for b in plan.buckets()))
+    srcs = None
+    if coords == zdo.WORLD:
+        srcs = list(reps)
+    elif torch.cuda.mem_get_info(dev)[0] >= D * N * 2 + (1 << 30):
+        srcs = [torch.zeros(N, dtype=torch.int16, device=dev) for _ in range(D)]
+    if srcs is None:
+        out["all_gather_params"] = {"skipped": "D whole parameter buffers do not fit beside the inputs"}
+        log("all_gather_params: skipped (device memory)")
+    else:
+        mine = srcs[plan.rank].clone()
+        srcs[plan.rank] = mine
+        t = timed(lambda: zdo.all_gather_params(plan, srcs, mine, stream))
+        nbytes = (N - ranges) * 4
+        out["all_gather_params"] = {"path": "in place into the rank's buffer", "elements_copied": N - ranges,
+                                    "bytes_per_element": 4, "kernel_avg_us": t * 1e6,
+                                    "achieved_gbps": nbytes / t / 1e9, "frac": nbytes / t / 1e9 / PEAK_HBM_GBPS}
+        log(f"all_gather_params: {t * 1e6:.1f} us, {nbytes / t / 1e9:.0f} GB/s algorithmic")
+        del mine
+    del srcs
 
     if coords == zdo.WORLD:
         N = plan.buffer_numel

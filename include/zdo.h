@@ -213,6 +213,23 @@ int sharded_adam_step_instances(const zdo_plan *plan, const uint16_t *const *gra
 int writeback_params(const zdo_plan *plan, const float *master, uint16_t *param_out,
                      int32_t param_coords, void *stream);
 
+/* Page 1, §4.4: after the step, every bucket's parameter buffer is
+ * all-gathered, so that every rank holds the whole updated parameters (the
+ * ZeRO-1 loop: reduce-scatter of the grads, sharded step, all-gather of the
+ * parameters). This is one rank's side of it: rank j's range of every padded
+ * bucket (padding included, as the collective over equal ranges moves it) is
+ * copied from params[j] into out. params: host array of n_params (== D)
+ * device pointers, bf16 parameter buffers of N elements in WORLD
+ * coordinates, params[j] holding rank j's write-back (e.g. sharded_adam_step
+ * or writeback_params with param_coords ZDO_WORLD). out: bf16, N elements;
+ * it may coincide exactly with one or more params[j] (in place, typically
+ * the plan's own rank: those ranges are already there and are not copied)
+ * and must not otherwise overlap any of them (ZDO_EALIAS). The plan may be
+ * any rank's: the bucket layout is the same for all. n_params != D:
+ * ZDO_EINVAL. */
+int all_gather_params(const zdo_plan *plan, const uint16_t *const *params, int32_t n_params,
+                      uint16_t *out, void *stream);
+
 /* ---- bucket by bucket ---------------------------------------------------------
  * Page 1, §2 and §4.2: a bucket's collective starts as soon as the grads of
  * its bucket are ready, bucket by bucket during the backward pass. These two

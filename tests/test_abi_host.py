@@ -27,7 +27,7 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     L = Z.require_library()
     names = header_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     assert sorted(Z.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -130,6 +130,7 @@ def test_launch_on_host_only_plan_is_an_error():
                                        None, None) == Z.EHIP
     assert L.sharded_adam_step_instances(plan.handle, reps, 1, 0, 1.0, 64, 80, 96, None, 0, ctypes.byref(hp), None,
                                          None) == Z.EHIP
+    assert L.all_gather_params(plan.handle, reps, 2, 48, None) == Z.EHIP
     assert b"device" in L.zdo_last_error()
     assert L.zdo_plan_norm_workspace_bytes(plan.handle) >= 8
     assert L.clip_coefficient(None, 1, 1.0, 64, None, None) == Z.EINVAL

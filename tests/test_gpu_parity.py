@@ -756,3 +756,80 @@ def test_instances_one_instance_is_the_plain_step(gpu):
         gpu.sharded_adam_step_instances(plan, [reps, reps[:7]], gpu.WORLD, 1.0, *st, None, gpu.WORLD, **hp)
     free()
 
+
+
+# ---- parameter all-gather ----------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(8))
+def test_all_gather_random_layouts(gpu, seed):
+    """Rank j's range of every padded bucket from params[j]: out of place into
+    a fresh buffer, and in place into a rank's own buffer (whose own ranges
+    are left as they are); the sources stay untouched."""
+    pr = random.Random(3000 + seed)
+    rng = np.random.default_rng(3000 + seed)
+    sizes, bucket, D = _random_layout(pr)
+    lay = OL.build_layout(sizes, bucket, D)
+    N = lay.buffer_numel
+    params_h = [bf16_host(rng, N, 1.0) for _ in range(D)]
+    params_d = [to_dev(x) for x in params_h]
+    plan = gpu.build_range_map(sizes, bucket, D, pr.randrange(D))
+    out = torch.full((max(N, 8),), SENTINEL, dtype=torch.int16, device=DEV)
+    gpu.all_gather_params(plan, params_d, out)
+    want = np.full(max(N, 8), SENTINEL, np.uint16)
+    OS.all_gather(lay, params_h, want)
+    assert_bf16(host_u16(out), want, "out of place")
+    for r in sorted({0, D - 1, pr.randrange(D)}):
+        bufs = [to_dev(x) for x in params_h]
+        gpu.all_gather_params(plan, bufs, bufs[r])
+        w = params_h[r].copy()
+        OS.all_gather(lay, params_h, w)
+        assert_bf16(host_u16(bufs[r]), w, f"in place r={r}")
+        for j in range(D):
+            if j != r:
+                assert_bf16(host_u16(bufs[j]), params_h[j], f"source {j} untouched")
+    free()
+
+
+@pytest.mark.parametrize("name", ["tiny", "frag"])
+def test_zero1_loop_step_then_all_gather(gpu, name):
+    """Page 1, §4.4: every rank steps its shard and writes back into its own
+    copy of the parameter buffer, then every rank all-gathers in place; all
+    D buffers end equal to the oracle's same loop, element for element."""
+    w = W.get(name)
+    lay = OL.build_layout(w.param_numel, w.bucket_numel, w.dp_size)
+    N, D = lay.buffer_numel, w.dp_size
+    rng = np.random.default_rng(41)
+    reps_d = _gen_world(w, N)
+    reps_h = [host_u16(x) for x in reps_d]
+    hpk = hp_kwargs(w.hp, 2)
+    hpa = ON.hp_array(w.hp, 2)
+    before = bf16_host(rng, N, 0.02)
+    bufs_d, bufs_h = [], []
+    for r in range(D):
+        plan = gpu.build_range_map(w.param_numel, w.bucket_numel, D, r)
+        st = _gen_state(w, plan.shard_numel)
+        st_h = [host_f32(x) for x in st]
+        pb_d, pb_h = to_dev(before), before.copy()
+        gpu.sharded_adam_step(plan, reps_d, gpu.WORLD, w.scale, *st, pb_d, gpu.WORLD, **hpk)
+        OS.rank_step(lay, r, reps_h, OS.WORLD, w.scale, *st_h, hpa, pb_h, OS.WORLD)
+        assert_bf16(host_u16(pb_d), pb_h, f"{name} r={r} write-back")
+        bufs_d.append(pb_d)
+        bufs_h.append(pb_h)
+        del st
+    want = before.copy()
+    OS.all_gather(lay, bufs_h, want)
+    for r in range(D):
+        gpu.all_gather_params(gpu.build_range_map(w.param_numel, w.bucket_numel, D, r), bufs_d, bufs_d[r])
+    for r in range(D):
+        assert_bf16(host_u16(bufs_d[r]), want, f"{name} rank {r} after the all-gather")
+    # argument checks
+    plan = gpu.build_range_map(w.param_numel, w.bucket_numel, D, 0)
+    with pytest.raises(gpu.ZdoError) as e:
+        gpu.all_gather_params(plan, bufs_d[:-1], bufs_d[0])
+    assert e.value.code == gpu.EINVAL
+    big = torch.zeros(N + 64, dtype=torch.int16, device=DEV)
+    with pytest.raises(gpu.ZdoError) as e:                               # overlaps without coinciding
+        gpu.all_gather_params(plan, [big[:N]] + bufs_d[1:], big[8:8 + N])
+    assert e.value.code == gpu.EALIAS
+    del reps_d, bufs_d
+    free()

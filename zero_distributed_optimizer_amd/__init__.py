@@ -68,7 +68,7 @@ EXPORTS = ("build_range_map", "zdo_plan_destroy", "zdo_plan_buffer_numel", "zdo_
            "zdo_plan_pieces", "reduce_scatter_local", "force_all_reduce", "sharded_adam_step",
            "writeback_params", "reduce_scatter_local_buckets", "sharded_adam_step_buckets",
            "zdo_plan_norm_workspace_bytes", "grad_norm_sq", "clip_coefficient", "sharded_adam_step_clipped",
-           "sharded_adam_step_instances", "zdo_device_copy", "zdo_last_error")
+           "sharded_adam_step_instances", "all_gather_params", "zdo_device_copy", "zdo_last_error")
 
 _lib = None
 
@@ -109,6 +109,7 @@ def require_library() -> ctypes.CDLL:
                                             vp, vp, vp]
     L.sharded_adam_step_instances.argtypes = [vp, vp, i32, i32, f32, vp, vp, vp, vp, i32, ctypes.POINTER(Adam), vp,
                                               vp]
+    L.all_gather_params.argtypes = [vp, vp, i32, vp, vp]
     L.zdo_device_copy.argtypes = [vp, vp, i64, vp]
     L.zdo_last_error.argtypes = []
     L.zdo_last_error.restype = ctypes.c_char_p
@@ -313,6 +314,14 @@ def sharded_adam_step_instances(plan: Plan, instances, grad_coords: int, scale: 
     _check(require_library().sharded_adam_step_instances(plan.handle, g, len(instances), grad_coords, scale, m, a, s,
                                                          p, param_coords, ctypes.byref(hp), mg,
                                                          _stream(stream, master.device)))
+
+
+def all_gather_params(plan: Plan, params, out, stream=None) -> None:
+    """Rank j's range of every padded bucket from params[j] (D bf16 buffers
+    of N elements, WORLD coordinates) into out; out may be one of them."""
+    p = _ptr_list(params, "params", plan.buffer_numel)
+    o = _dev_ptr(out, "out", "bf16", plan.buffer_numel)
+    _check(require_library().all_gather_params(plan.handle, p, len(params), o, _stream(stream, out.device)))
 
 
 def grad_norm_sq(plan: Plan, replicas, replica_coords: int, scale: float, workspace, norm_sq_out,

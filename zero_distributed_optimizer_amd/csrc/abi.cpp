@@ -537,6 +537,33 @@ int writeback_params(const zdo_plan *plan, const float *master, uint16_t *param_
     return launch_result(launch_writeback(a, plan->lds_per_cu, static_cast<hipStream_t>(stream)), fn);
 }
 
+int all_gather_params(const zdo_plan *plan, const uint16_t *const *params, int32_t n_params, uint16_t *out,
+                      void *stream) {
+    const char *fn = "all_gather_params";
+    if (int rc = check_plan(plan, fn))
+        return rc;
+    if (n_params != plan->dp_size)
+        return fail(ZDO_EINVAL, std::string(fn) + ": n_params must equal the DP size " +
+                                    std::to_string(plan->dp_size));
+    GatherArgs a{};
+    Span spans[ZDO_MAX_REPLICAS];
+    if (int rc = take_replicas(plan, params, n_params, ZDO_WORLD, fn, a.src, spans))
+        return rc;
+    if (int rc = check_ptr(out, fn, "out"))
+        return rc;
+    const Span so = span_of(out, plan->buffer_numel, 2);
+    for (int32_t j = 0; j < n_params; ++j)
+        if (overlap(so, spans[j]) && out != params[j])
+            return fail(ZDO_EALIAS, std::string(fn) + ": out overlaps params[" + std::to_string(j) +
+                                        "] without coinciding with it");
+    a.ranges = plan->d_gather_ranges;
+    a.group = plan->d_gather_group;
+    a.nranges = int64_t(plan->gather_ranges.size());
+    a.ntiles = plan->gather_tiles;
+    a.out = out;
+    return launch_result(launch_gather(a, static_cast<hipStream_t>(stream)), fn);
+}
+
 int zdo_device_copy(void *dst, const void *src, int64_t bytes, void *stream) {
     const char *fn = "zdo_device_copy";
     if (bytes < 0 || bytes % 16 != 0)

@@ -64,6 +64,18 @@ struct NormArgs {
     double *partial;     // one per tile of walk
 };
 
+// The all-gather of the parameter buffers: every rank range of every padded
+// bucket copied from its rank's buffer into out, except ranges whose source
+// is out itself.
+struct GatherArgs {
+    const RangeSpan *ranges;
+    const uint32_t *group;   // range at the first tile of every kGatherGroup tiles
+    int64_t nranges;         // buckets x D
+    int64_t ntiles;
+    const uint16_t *src[ZDO_MAX_REPLICAS];
+    uint16_t *out;
+};
+
 struct WritebackArgs {
     Walk walk;
     int32_t param_local;
@@ -77,6 +89,7 @@ hipError_t launch_reduce(const ReduceArgs &a, int lds_per_cu, hipStream_t stream
 hipError_t launch_step(const StepArgs &a, int lds_per_cu, hipStream_t stream);
 hipError_t launch_writeback(const WritebackArgs &a, int lds_per_cu, hipStream_t stream);
 hipError_t launch_copy(void *dst, const void *src, int64_t n16, hipStream_t stream);
+hipError_t launch_gather(const GatherArgs &a, hipStream_t stream);
 // Squared norm: per-tile partials into a.partial, then their fixed-order sum
 // into *norm_sq (0 when a.walk has no tiles).
 hipError_t launch_norm(const NormArgs &a, double *norm_sq, int lds_per_cu, hipStream_t stream);

@@ -552,6 +552,49 @@ __global__ __launch_bounds__(kBlock) void writeback_kernel(WritebackArgs a) {
     }
 }
 
+// ---- parameter all-gather ---------------------------------------------------------------------
+// One tile space over every rank range of every padded bucket, with no empty
+// tiles: tile -> range through the coarse group index, then the range's own
+// entry. A tile is kGatherTile elements from the range's start rounded down
+// to 64; lane l takes the chunks l, l + 64, l + 128, l + 192 (8 elements
+// each), so each load instruction covers 1 KiB and the tile's four loads
+// are in flight together. A range whose source is `out` itself is already
+// in place and is skipped. Every byte is read once and written once:
+// non-temporal loads and stores, as in the copy.
+constexpr int kGatherChunks = int(kGatherTile / kTileElems);   // chunks per lane
+
+__global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a) {
+    for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+        int64_t y = a.group[tile / kGatherGroup];
+        while (y + 1 < a.nranges && a.ranges[y + 1].tile0 <= tile)
+            ++y;
+        const RangeSpan r = a.ranges[y];
+        const uint16_t *src = a.src[r.src];
+        if (src == a.out)
+            continue;
+        const int64_t base = tile_origin(r.rb) + (tile - r.tile0) * kGatherTile;
+        u32x4 v[kGatherChunks];
+        bool whole[kGatherChunks];
+#pragma unroll
+        for (int c = 0; c < kGatherChunks; ++c) {
+            const int64_t w0 = base + (int64_t(c) * kBlock + threadIdx.x) * kChunk;
+            whole[c] = w0 >= r.rb && w0 + kChunk <= r.re;
+            if (whole[c])
+                v[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + w0));
+        }
+#pragma unroll
+        for (int c = 0; c < kGatherChunks; ++c) {
+            const int64_t w0 = base + (int64_t(c) * kBlock + threadIdx.x) * kChunk;
+            if (whole[c]) {
+                __builtin_nontemporal_store(v[c], reinterpret_cast<u32x4 *>(a.out + w0));
+            } else {
+                for (int64_t w = w0 > r.rb ? w0 : r.rb; w < w0 + kChunk && w < r.re; ++w)
+                    a.out[w] = src[w];
+            }
+        }
+    }
+}
+
 __global__ __launch_bounds__(kBlock) void copy_kernel(u32x4 *dst, const u32x4 *src, int64_t n16) {
     for (int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x; i < n16; i += int64_t(gridDim.x) * kBlock)
         __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
@@ -685,6 +728,15 @@ hipError_t launch_norm(const NormArgs &a, double *norm_sq, int lds_per_cu, hipSt
 hipError_t launch_clip(const double *parts, int32_t n, float max_norm, float *coeff, double *norm_out,
                        hipStream_t stream) {
     hipLaunchKernelGGL(clip_kernel, dim3(1), dim3(64), 0, stream, parts, n, max_norm, coeff, norm_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherArgs &a, hipStream_t stream) {
+    if (a.ntiles <= 0)
+        return hipSuccess;
+    // 4 KiB read per tile, against 10-40 KiB in the step: no occupancy cap
+    // (as the copy), so that enough bytes are in flight
+    hipLaunchKernelGGL(gather_kernel, dim3(grid_for(a.ntiles)), dim3(kBlock), 0, stream, a);
     return hipGetLastError();
 }
 

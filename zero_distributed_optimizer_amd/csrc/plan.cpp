@@ -131,6 +131,14 @@ int build_plan(const int64_t *param_numel, int32_t n_params, int64_t bucket_nume
         }
         (segs == &p.param_segs ? p.param_tiles : p.range_tiles) = t;
     }
+    int64_t gt = 0;
+    for (const auto &b : p.buckets)
+        for (int32_t j = 0; j < dp_size; ++j) {
+            const int64_t rb = b.offset + int64_t(j) * b.shard_numel;
+            p.gather_ranges.push_back({rb, rb + b.shard_numel, gt, j});
+            gt += range_tiles(rb, b.shard_numel);
+        }
+    p.gather_tiles = gt;
     return ZDO_OK;
 }
 
@@ -153,14 +161,32 @@ int upload_plan(zdo_plan &p) {
             const int64_t nt = seg_tiles((*segs)[s].wbeg, (*segs)[s].len);
             tile_seg.insert(tile_seg.end(), size_t(nt), uint32_t(s));
         }
+    // all-gather: the range holding the first tile of every kGatherGroup tiles
+    std::vector<uint32_t> group(size_t((p.gather_tiles + kGatherGroup - 1) / kGatherGroup));
+    {
+        size_t y = 0;
+        for (size_t g = 0; g < group.size(); ++g) {
+            const int64_t tile = int64_t(g) * kGatherGroup;
+            while (y + 1 < p.gather_ranges.size() && p.gather_ranges[y + 1].tile0 <= tile)
+                ++y;
+            group[g] = uint32_t(y);
+        }
+    }
+    // one allocation: segments, gather ranges, then the two uint32 tables
     const size_t nseg = p.param_segs.size() + p.range_segs.size();
     const size_t seg_bytes = nseg * sizeof(Seg);
-    const size_t bytes = seg_bytes + tile_seg.size() * sizeof(uint32_t);
+    const size_t span_bytes = p.gather_ranges.size() * sizeof(RangeSpan);
+    const size_t tile_bytes = tile_seg.size() * sizeof(uint32_t);
+    const size_t bytes = seg_bytes + span_bytes + tile_bytes + group.size() * sizeof(uint32_t);
     std::vector<char> host(bytes);
     std::copy(p.param_segs.begin(), p.param_segs.end(), reinterpret_cast<Seg *>(host.data()));
     std::copy(p.range_segs.begin(), p.range_segs.end(),
               reinterpret_cast<Seg *>(host.data()) + p.param_segs.size());
-    std::copy(tile_seg.begin(), tile_seg.end(), reinterpret_cast<uint32_t *>(host.data() + seg_bytes));
+    std::copy(p.gather_ranges.begin(), p.gather_ranges.end(),
+              reinterpret_cast<RangeSpan *>(host.data() + seg_bytes));
+    std::copy(tile_seg.begin(), tile_seg.end(), reinterpret_cast<uint32_t *>(host.data() + seg_bytes + span_bytes));
+    std::copy(group.begin(), group.end(),
+              reinterpret_cast<uint32_t *>(host.data() + seg_bytes + span_bytes + tile_bytes));
     void *d = nullptr;
     hipError_t e = hipMalloc(&d, bytes);
     if (e != hipSuccess) {
@@ -177,8 +203,10 @@ int upload_plan(zdo_plan &p) {
     p.d_table = d;
     p.d_param_segs = static_cast<const Seg *>(d);
     p.d_range_segs = p.d_param_segs + p.param_segs.size();
-    p.d_param_tile_seg = reinterpret_cast<const uint32_t *>(static_cast<const char *>(d) + seg_bytes);
+    p.d_gather_ranges = reinterpret_cast<const RangeSpan *>(static_cast<const char *>(d) + seg_bytes);
+    p.d_param_tile_seg = reinterpret_cast<const uint32_t *>(static_cast<const char *>(d) + seg_bytes + span_bytes);
     p.d_range_tile_seg = p.d_param_tile_seg + p.param_tiles;
+    p.d_gather_group = p.d_range_tile_seg + p.range_tiles;
     p.device = dev;
     if (hipDeviceGetAttribute(&p.lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
         hipSuccess) {

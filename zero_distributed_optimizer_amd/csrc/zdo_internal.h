@@ -37,6 +37,23 @@ inline int64_t seg_tiles(int64_t wbeg, int64_t len) {
     return (wbeg + len - tile_origin(wbeg) + kTileElems - 1) / kTileElems;
 }
 
+// One rank range of one padded bucket, as the all-gather walks it: tiles of
+// kGatherTile elements from rb rounded down to kAnchor.
+struct RangeSpan {
+    int64_t rb, re;  // WORLD range [rb, re)
+    int64_t tile0;   // its first tile in the all-gather's tile space
+    int64_t src;     // the rank whose buffer holds it
+};
+// All-gather tiles: 2048 elements, four 16-byte chunks per lane, so that the
+// tile's lookups are paid once per 4 KiB read. The tile space maps to ranges
+// through one entry per kGatherGroup tiles (the range holding the group's
+// first tile; later ranges of the group follow by their tile0).
+constexpr int64_t kGatherTile = 2048;
+constexpr int64_t kGatherGroup = 64;
+inline int64_t range_tiles(int64_t rb, int64_t len) {
+    return (rb + len - tile_origin(rb) + kGatherTile - 1) / kGatherTile;
+}
+
 void set_error(const std::string &msg);
 
 }  // namespace zdo
@@ -55,11 +72,17 @@ struct zdo_plan {
     std::vector<zdo::Seg> param_segs, range_segs;
     std::vector<int32_t> param_seg_bucket;   // bucket of each param seg (range seg i is bucket i)
     int64_t param_tiles = 0, range_tiles = 0;
+    // The all-gather's launch space: every rank range of every padded bucket
+    // (bucket-major, rank-minor).
+    std::vector<zdo::RangeSpan> gather_ranges;
+    int64_t gather_tiles = 0;
     // Device copies, in one allocation on `device`: both segment lists and,
     // for every tile of each launch space, the index of its segment.
     void *d_table = nullptr;
     const zdo::Seg *d_param_segs = nullptr, *d_range_segs = nullptr;
     const uint32_t *d_param_tile_seg = nullptr, *d_range_tile_seg = nullptr;
+    const zdo::RangeSpan *d_gather_ranges = nullptr;
+    const uint32_t *d_gather_group = nullptr;
     int device = -1;
     int lds_per_cu = 0;   // bytes of LDS per compute unit on `device`
 };

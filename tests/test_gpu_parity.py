@@ -833,3 +833,87 @@ def test_zero1_loop_step_then_all_gather(gpu, name):
     assert e.value.code == gpu.EALIAS
     del reps_d, bufs_d
     free()
+
+
+@pytest.mark.parametrize("off_bytes", [16, 48])
+def test_buffers_off_the_cache_line(gpu, off_bytes):
+    """The ABI asks for 16-byte alignment only; the kernels' tiles are laid
+    out for 128-byte lines. Every buffer here starts off_bytes past a line:
+    reduce-scatter, the fused step, the clipped path and the all-gather stay
+    bit-exact against the oracle."""
+    rng = np.random.default_rng(off_bytes)
+    sizes, bucket, D = [5000, 13, 20000, 1, 4097, 777], 9000, 4
+    lay = OL.build_layout(sizes, bucket, D)
+    N = lay.buffer_numel
+
+    def view(n, dtype, fill):
+        per = off_bytes // (2 if dtype == torch.int16 else 4)
+        big = torch.full((n + per + 64,), fill, dtype=dtype, device=DEV)
+        v = big[per:per + n]
+        assert v.data_ptr() % 128 == off_bytes
+        return v
+
+    reps_h = [bf16_host(rng, N) for _ in range(D)]
+    reps_d = []
+    for x in reps_h:
+        v = view(N, torch.int16, 0)
+        v.copy_(to_dev(x))
+        reps_d.append(v)
+    hp = W.get("tiny").hp
+    r = 2
+    plan = gpu.build_range_map(sizes, bucket, D, r)
+    Ln = plan.shard_numel
+    # reduce-scatter
+    out = view(Ln, torch.int16, SENTINEL)
+    gpu.reduce_scatter_local(plan, reps_d, gpu.WORLD, 0.25, out, gpu.LOCAL)
+    want = np.full(Ln, SENTINEL, np.uint16)
+    OS.reduce_scatter(lay, r, reps_h, OS.WORLD, 0.25, want, OS.LOCAL)
+    assert_bf16(host_u16(out), want, "reduce-scatter")
+    # fused step
+    st_h = [(rng.standard_normal(Ln) * 0.02).astype(np.float32), np.zeros(Ln, np.float32),
+            np.zeros(Ln, np.float32)]
+    st = []
+    for x in st_h:
+        v = view(Ln, torch.float32, 0.0)
+        v.copy_(to_dev(x))
+        st.append(v)
+    par = view(N, torch.int16, SENTINEL)
+    mg = view(Ln, torch.float32, -7.0)
+    gpu.sharded_adam_step(plan, reps_d, gpu.WORLD, 0.25, *st, par, gpu.WORLD, main_grad_out=mg, **hp_kwargs(hp, 1))
+    want_st = [x.copy() for x in st_h]
+    want_par = np.full(N, SENTINEL, np.uint16)
+    want_mg = np.full(Ln, -7.0, np.float32)
+    OS.rank_step(lay, r, reps_h, OS.WORLD, 0.25, *want_st, ON.hp_array(hp, 1), want_par, OS.WORLD, want_mg)
+    for got, w_, nm in zip(st, want_st, ("master", "exp_avg", "exp_avg_sq")):
+        assert_f32(host_f32(got), w_, nm)
+    assert_bf16(host_u16(par), want_par, "params")
+    assert_f32(host_f32(mg), want_mg, "main grad")
+    # clipped path from the reduced gradient
+    ws = torch.empty(plan.norm_workspace_bytes + off_bytes, dtype=torch.uint8, device=DEV)[off_bytes:]
+    parts = torch.zeros(1, dtype=torch.float64, device=DEV)
+    red = view(Ln, torch.int16, 0)
+    gpu.grad_norm_sq(plan, reps_d, gpu.WORLD, 0.25, ws, parts, red, gpu.LOCAL)
+    coeff = torch.empty(1, dtype=torch.float32, device=DEV)
+    gpu.clip_coefficient(parts, 0.01, coeff)
+    c = float(coeff.item())
+    st2 = [view(Ln, torch.float32, 0.0) for _ in range(3)]
+    for v, x in zip(st2, st_h):
+        v.copy_(to_dev(x))
+    gpu.sharded_adam_step_clipped(plan, [red], gpu.LOCAL, 1.0, *st2, None, gpu.WORLD, grad_coeff=coeff,
+                                  **hp_kwargs(hp, 1))
+    want2 = [x.copy() for x in st_h]
+    OS.rank_step(lay, r, reps_h, OS.WORLD, 0.25, *want2, ON.hp_array(hp, 1), grad_coeff=c)
+    for got, w_, nm in zip(st2, want2, ("master", "exp_avg", "exp_avg_sq")):
+        assert_f32(host_f32(got), w_, nm + " (clipped)")
+    # all-gather in place into rank r's buffer
+    bufs_h = [bf16_host(rng, N) for _ in range(D)]
+    bufs = []
+    for x in bufs_h:
+        v = view(N, torch.int16, 0)
+        v.copy_(to_dev(x))
+        bufs.append(v)
+    gpu.all_gather_params(plan, bufs, bufs[r])
+    want_g = bufs_h[r].copy()
+    OS.all_gather(lay, bufs_h, want_g)
+    assert_bf16(host_u16(bufs[r]), want_g, "all-gather")
+    free()

@@ -20,7 +20,6 @@ struct Walk {
     const uint32_t *tile_seg;
     int64_t ntiles;      // tiles in this launch
     int64_t flat_numel;
-    int64_t nseg;
     int64_t tile_begin;  // first tile of this launch (a bucket range starts past 0)
 };
 

@@ -1,23 +1,25 @@
 // Device kernels for gfx950 (CDNA4): the fused sharded Adam step, the
-// reduce-scatter / all-reduce of the D contributions, the parameter
-// write-back and a plain copy.
+// reduce-scatter / all-reduce of the D contributions, the squared gradient
+// norm and clipping coefficient, the parameter write-back, the parameter
+// all-gather and a plain copy.
 //
-// The step is a pure stream over the rank's elements: (2D + 26) bytes per
-// element against a few dozen VALU operations, so it is bound by HBM
-// bandwidth, not by the matrix cores. A LOCAL index is congruent to its
-// WORLD index modulo 64, and a segment's tiles start at a multiple of 64
-// WORLD elements, so with 128-byte-aligned buffers every stream crosses cache
-// lines at tile boundaries only (no line is fetched by two workgroups). A
-// workgroup is a single wave and takes a tile of 512 consecutive elements of
-// one segment: 1 KiB of every bf16 stream and 2 KiB of every fp32 stream,
-// contiguously. In the reduce, norm and write-back
-// kernels lane l takes the 8-element chunk [8l, 8l + 8) of the tile (one
-// 16-byte load per bf16 stream); the step takes two quads per lane (see
+// Every kernel is a stream: the step moves (2D + 26) bytes per element
+// against a few dozen VALU operations, so it is bound by HBM bandwidth, not
+// by the matrix cores. A LOCAL index is congruent to its WORLD index modulo
+// 64, and a segment's tiles start at a multiple of 64 WORLD elements, so
+// with 128-byte-aligned buffers every stream crosses cache lines at tile
+// boundaries only (no line is fetched by two workgroups). A workgroup is a
+// single wave and takes a tile of 512 consecutive elements of one segment:
+// 1 KiB of every bf16 stream and 2 KiB of every fp32 stream, contiguously.
+// In the reduce, norm and write-back kernels lane l takes the 8-element
+// chunk [8l, 8l + 8) of the tile (one 16-byte load per bf16 stream); the
+// step takes two quads per lane and the all-gather 2048-element tiles (see
 // there). Chunks or quads cut by a segment's ends take a per-element path.
 //
 // HBM serves this mix of many read streams and some write streams best when
-// few requestors share it: one-wave workgroups, a capped number per compute
-// unit, non-temporal loads (every byte is read once).
+// few requestors share it: one-wave workgroups, a number per compute unit
+// capped by the launch's length (see lds_reserve), non-temporal loads of
+// what is read once.
 //
 // Arithmetic is fixed (contraction off, IEEE division and square root,
 // fp32 subnormals kept) so that results match a sequential CPU evaluation bit

@@ -9,7 +9,8 @@
 
 namespace zdo {
 
-// A lane works on chunks of 8 consecutive elements: 16 bytes of bf16, 32 of fp32.
+// Elements per lane per tile: 8 (a 16-byte bf16 chunk, or two 4-element
+// quads in the step).
 constexpr int kChunk = 8;
 // Threads per workgroup; a workgroup takes one tile of kBlock chunks at a time.
 #ifndef ZDO_BLOCK

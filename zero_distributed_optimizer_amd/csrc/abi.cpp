@@ -242,7 +242,7 @@ static int reduce_scatter_impl(const char *fn, const zdo_plan *plan, int32_t b0,
                                         " without coinciding with it");
     int64_t first = 0, count = 0;
     bucket_tiles(plan->range_segs, nullptr, plan->range_tiles, b0, b1, first, count);
-    a.walk = {plan->d_range_segs, plan->d_range_tile_seg, count, 0, first};
+    a.walk = {plan->d_range_segs, plan->d_range_group, int64_t(plan->range_segs.size()), count, 0, first};
     a.nrep = n_replicas;
     a.in_local = replica_coords == ZDO_LOCAL;
     a.out_local = out_coords == ZDO_LOCAL;
@@ -291,7 +291,7 @@ int force_all_reduce(const zdo_plan *plan, const uint16_t *const *replicas, int3
         if (overlap(so, spans[j]) && out_full != replicas[j])
             return fail(ZDO_EALIAS, std::string(fn) + ": out_full overlaps replica " + std::to_string(j) +
                                         " without coinciding with it");
-    a.walk = {nullptr, nullptr, seg_tiles(0, plan->buffer_numel), plan->buffer_numel, 0};
+    a.walk = {nullptr, nullptr, 0, seg_tiles(0, plan->buffer_numel), plan->buffer_numel, 0};
     a.nrep = n_replicas;
     a.in_local = 0;
     a.out_local = 0;
@@ -372,7 +372,7 @@ static int adam_step(const char *fn, const zdo_plan *plan, int32_t b0, int32_t b
     }
     int64_t first = 0, count = 0;
     bucket_tiles(plan->param_segs, plan->param_seg_bucket.data(), plan->param_tiles, b0, b1, first, count);
-    a.walk = {plan->d_param_segs, plan->d_param_tile_seg, count, 0, first};
+    a.walk = {plan->d_param_segs, plan->d_param_group, int64_t(plan->param_segs.size()), count, 0, first};
     a.nrep = n_grads;
     a.ninst = n_instances;
     a.dinst = n_grads / n_instances;
@@ -489,7 +489,7 @@ int grad_norm_sq(const zdo_plan *plan, const uint16_t *const *replicas, int32_t 
                 return fail(ZDO_EALIAS, std::string(fn) + ": reduced_out overlaps replica " + std::to_string(j) +
                                             " without coinciding with it");
     }
-    a.walk = {plan->d_param_segs, plan->d_param_tile_seg, plan->param_tiles, 0, 0};
+    a.walk = {plan->d_param_segs, plan->d_param_group, int64_t(plan->param_segs.size()), plan->param_tiles, 0, 0};
     a.nrep = n_replicas;
     a.in_local = replica_coords == ZDO_LOCAL;
     a.out_local = out_coords == ZDO_LOCAL;
@@ -530,7 +530,7 @@ int writeback_params(const zdo_plan *plan, const float *master, uint16_t *param_
     if (overlap(span_of(master, plan->shard_numel, 4), span_of(param_out, extent(plan, param_coords), 2)))
         return fail(ZDO_EALIAS, std::string(fn) + ": param_out overlaps master");
     WritebackArgs a{};
-    a.walk = {plan->d_param_segs, plan->d_param_tile_seg, plan->param_tiles, 0, 0};
+    a.walk = {plan->d_param_segs, plan->d_param_group, int64_t(plan->param_segs.size()), plan->param_tiles, 0, 0};
     a.param_local = param_coords == ZDO_LOCAL;
     a.master = master;
     a.param = param_out;

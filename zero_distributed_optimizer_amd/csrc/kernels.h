@@ -12,12 +12,14 @@ struct AdamConst {
     float lr, b1, b2, omb1, omb2, eps, wd, bc1, bc2;
 };
 
-// Segments walked by a launch: either a table (segs + per-tile segment
-// index), of which the launch takes tiles [tile_begin, tile_begin + ntiles),
-// or, when segs is NULL, the single run [0, flat_numel).
+// Segments walked by a launch: either a table (nseg segments and their
+// kTileGroup index), of which the launch takes tiles [tile_begin,
+// tile_begin + ntiles), or, when segs is NULL, the single run
+// [0, flat_numel).
 struct Walk {
     const Seg *segs;
-    const uint32_t *tile_seg;
+    const uint32_t *group;
+    int64_t nseg;
     int64_t ntiles;      // tiles in this launch
     int64_t flat_numel;
     int64_t tile_begin;  // first tile of this launch (a bucket range starts past 0)
@@ -68,7 +70,7 @@ struct NormArgs {
 // is out itself.
 struct GatherArgs {
     const RangeSpan *ranges;
-    const uint32_t *group;   // range at the first tile of every kGatherGroup tiles
+    const uint32_t *group;   // range at the first tile of every kTileGroup tiles
     int64_t nranges;         // buckets x D
     int64_t ntiles;
     const uint16_t *src[ZDO_MAX_REPLICAS];

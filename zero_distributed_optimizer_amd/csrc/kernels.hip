@@ -72,16 +72,31 @@ struct ChunkPos {
     int lo, hi;     // the chunk's slots [lo, hi) that belong to the segment
 };
 
+// The segment holding `tile` (a table walk): its group's entry, then the
+// later segments of the group by their first tile.
+__device__ __forceinline__ Seg seg_of(const Walk &wk, int64_t tile) {
+    int64_t si = wk.group[tile / kTileGroup];
+    Seg cur = wk.segs[si];
+    while (si + 1 < wk.nseg) {
+        const Seg nxt = wk.segs[si + 1];
+        if (nxt.tile0 > tile)
+            break;
+        cur = nxt;
+        ++si;
+    }
+    return cur;
+}
+
 // The chunk this thread takes in `tile`; false if it holds no element of the
 // segment.
 __device__ __forceinline__ bool chunk_of(const Walk &wk, int64_t tile, ChunkPos &c) {
     int64_t wbeg, lbeg, len, tile0;
     if (wk.segs) {
-        const Seg *s = wk.segs + wk.tile_seg[tile];
-        wbeg = s->wbeg;
-        lbeg = s->lbeg;
-        len = s->len;
-        tile0 = s->tile0;
+        const Seg s = seg_of(wk, tile);
+        wbeg = s.wbeg;
+        lbeg = s.lbeg;
+        len = s.len;
+        tile0 = s.tile0;
     } else {
         wbeg = 0;
         lbeg = 0;
@@ -236,11 +251,11 @@ struct Quad {
 __device__ __forceinline__ void quads_of(const Walk &wk, int64_t tile, Quad q[2]) {
     int64_t wbeg, lbeg, len, tile0;
     if (wk.segs) {
-        const Seg *s = wk.segs + wk.tile_seg[tile];
-        wbeg = s->wbeg;
-        lbeg = s->lbeg;
-        len = s->len;
-        tile0 = s->tile0;
+        const Seg s = seg_of(wk, tile);
+        wbeg = s.wbeg;
+        lbeg = s.lbeg;
+        len = s.len;
+        tile0 = s.tile0;
     } else {
         wbeg = 0;
         lbeg = 0;
@@ -556,7 +571,7 @@ __global__ __launch_bounds__(kBlock) void writeback_kernel(WritebackArgs a) {
 
 // ---- parameter all-gather ---------------------------------------------------------------------
 // One tile space over every rank range of every padded bucket, with no empty
-// tiles: tile -> range through the coarse group index, then the range's own
+// tiles: tile -> range through the kTileGroup index, then the range's own
 // entry. A tile is kGatherTile elements from the range's start rounded down
 // to 64; lane l takes the chunks l, l + 64, l + 128, l + 192 (8 elements
 // each), so each load instruction covers 1 KiB and the tile's four loads
@@ -567,7 +582,7 @@ constexpr int kGatherChunks = int(kGatherTile / kTileElems);   // chunks per lan
 
 __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a) {
     for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
-        int64_t y = a.group[tile / kGatherGroup];
+        int64_t y = a.group[tile / kTileGroup];
         while (y + 1 < a.nranges && a.ranges[y + 1].tile0 <= tile)
             ++y;
         const RangeSpan r = a.ranges[y];

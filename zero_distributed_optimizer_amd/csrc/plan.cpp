@@ -153,40 +153,40 @@ int upload_plan(zdo_plan &p) {
         set_error("build_range_map: hipGetDevice failed");
         return ZDO_EHIP;
     }
-    // tile -> segment index of each launch space
-    std::vector<uint32_t> tile_seg;
-    tile_seg.reserve(size_t(p.param_tiles + p.range_tiles));
-    for (const auto *segs : {&p.param_segs, &p.range_segs})
-        for (size_t s = 0; s < segs->size(); ++s) {
-            const int64_t nt = seg_tiles((*segs)[s].wbeg, (*segs)[s].len);
-            tile_seg.insert(tile_seg.end(), size_t(nt), uint32_t(s));
+    // per launch space, the segment holding the first tile of every
+    // kTileGroup tiles
+    auto group_index = [](int64_t ntiles, size_t n, auto tile0_of) {
+        std::vector<uint32_t> g(size_t((ntiles + kTileGroup - 1) / kTileGroup));
+        size_t s = 0;
+        for (size_t i = 0; i < g.size(); ++i) {
+            while (s + 1 < n && tile0_of(s + 1) <= int64_t(i) * kTileGroup)
+                ++s;
+            g[i] = uint32_t(s);
         }
-    // all-gather: the range holding the first tile of every kGatherGroup tiles
-    std::vector<uint32_t> group(size_t((p.gather_tiles + kGatherGroup - 1) / kGatherGroup));
-    {
-        size_t y = 0;
-        for (size_t g = 0; g < group.size(); ++g) {
-            const int64_t tile = int64_t(g) * kGatherGroup;
-            while (y + 1 < p.gather_ranges.size() && p.gather_ranges[y + 1].tile0 <= tile)
-                ++y;
-            group[g] = uint32_t(y);
-        }
-    }
-    // one allocation: segments, gather ranges, then the two uint32 tables
+        return g;
+    };
+    const auto param_group =
+        group_index(p.param_tiles, p.param_segs.size(), [&](size_t s) { return p.param_segs[s].tile0; });
+    const auto range_group =
+        group_index(p.range_tiles, p.range_segs.size(), [&](size_t s) { return p.range_segs[s].tile0; });
+    const auto gather_group =
+        group_index(p.gather_tiles, p.gather_ranges.size(), [&](size_t y) { return p.gather_ranges[y].tile0; });
+    // one allocation: segments, gather ranges, then the three group indexes
     const size_t nseg = p.param_segs.size() + p.range_segs.size();
     const size_t seg_bytes = nseg * sizeof(Seg);
     const size_t span_bytes = p.gather_ranges.size() * sizeof(RangeSpan);
-    const size_t tile_bytes = tile_seg.size() * sizeof(uint32_t);
-    const size_t bytes = seg_bytes + span_bytes + tile_bytes + group.size() * sizeof(uint32_t);
+    const size_t ngroup = param_group.size() + range_group.size() + gather_group.size();
+    const size_t bytes = seg_bytes + span_bytes + ngroup * sizeof(uint32_t);
     std::vector<char> host(bytes);
     std::copy(p.param_segs.begin(), p.param_segs.end(), reinterpret_cast<Seg *>(host.data()));
     std::copy(p.range_segs.begin(), p.range_segs.end(),
               reinterpret_cast<Seg *>(host.data()) + p.param_segs.size());
     std::copy(p.gather_ranges.begin(), p.gather_ranges.end(),
               reinterpret_cast<RangeSpan *>(host.data() + seg_bytes));
-    std::copy(tile_seg.begin(), tile_seg.end(), reinterpret_cast<uint32_t *>(host.data() + seg_bytes + span_bytes));
-    std::copy(group.begin(), group.end(),
-              reinterpret_cast<uint32_t *>(host.data() + seg_bytes + span_bytes + tile_bytes));
+    uint32_t *gi = reinterpret_cast<uint32_t *>(host.data() + seg_bytes + span_bytes);
+    gi = std::copy(param_group.begin(), param_group.end(), gi);
+    gi = std::copy(range_group.begin(), range_group.end(), gi);
+    std::copy(gather_group.begin(), gather_group.end(), gi);
     void *d = nullptr;
     hipError_t e = hipMalloc(&d, bytes);
     if (e != hipSuccess) {
@@ -204,9 +204,9 @@ int upload_plan(zdo_plan &p) {
     p.d_param_segs = static_cast<const Seg *>(d);
     p.d_range_segs = p.d_param_segs + p.param_segs.size();
     p.d_gather_ranges = reinterpret_cast<const RangeSpan *>(static_cast<const char *>(d) + seg_bytes);
-    p.d_param_tile_seg = reinterpret_cast<const uint32_t *>(static_cast<const char *>(d) + seg_bytes + span_bytes);
-    p.d_range_tile_seg = p.d_param_tile_seg + p.param_tiles;
-    p.d_gather_group = p.d_range_tile_seg + p.range_tiles;
+    p.d_param_group = reinterpret_cast<const uint32_t *>(static_cast<const char *>(d) + seg_bytes + span_bytes);
+    p.d_range_group = p.d_param_group + param_group.size();
+    p.d_gather_group = p.d_range_group + range_group.size();
     p.device = dev;
     if (hipDeviceGetAttribute(&p.lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
         hipSuccess) {

@@ -37,6 +37,11 @@ constexpr int64_t tile_origin(int64_t wbeg) { return wbeg / kAnchor * kAnchor; }
 inline int64_t seg_tiles(int64_t wbeg, int64_t len) {
     return (wbeg + len - tile_origin(wbeg) + kTileElems - 1) / kTileElems;
 }
+// Tiles map to their segment (or range) through one entry per kTileGroup
+// tiles: the one holding the group's first tile; the few later ones of the
+// group follow by their tile0. The index stays small enough to live in the
+// L2 cache (4 bytes per 64 tiles), so a tile's lookup does not go to HBM.
+constexpr int64_t kTileGroup = 64;
 
 // One rank range of one padded bucket, as the all-gather walks it: tiles of
 // kGatherTile elements from rb rounded down to kAnchor.
@@ -46,11 +51,9 @@ struct RangeSpan {
     int64_t src;     // the rank whose buffer holds it
 };
 // All-gather tiles: 2048 elements, four 16-byte chunks per lane, so that the
-// tile's lookups are paid once per 4 KiB read. The tile space maps to ranges
-// through one entry per kGatherGroup tiles (the range holding the group's
-// first tile; later ranges of the group follow by their tile0).
+// tile's lookups are paid once per 4 KiB read. They map to ranges through a
+// kTileGroup index as above.
 constexpr int64_t kGatherTile = 2048;
-constexpr int64_t kGatherGroup = 64;
 inline int64_t range_tiles(int64_t rb, int64_t len) {
     return (rb + len - tile_origin(rb) + kGatherTile - 1) / kGatherTile;
 }
@@ -77,11 +80,11 @@ struct zdo_plan {
     // (bucket-major, rank-minor).
     std::vector<zdo::RangeSpan> gather_ranges;
     int64_t gather_tiles = 0;
-    // Device copies, in one allocation on `device`: both segment lists and,
-    // for every tile of each launch space, the index of its segment.
+    // Device copies, in one allocation on `device`: both segment lists, the
+    // gather ranges, and the kTileGroup index of each launch space.
     void *d_table = nullptr;
     const zdo::Seg *d_param_segs = nullptr, *d_range_segs = nullptr;
-    const uint32_t *d_param_tile_seg = nullptr, *d_range_tile_seg = nullptr;
+    const uint32_t *d_param_group = nullptr, *d_range_group = nullptr;
     const zdo::RangeSpan *d_gather_ranges = nullptr;
     const uint32_t *d_gather_group = nullptr;
     int device = -1;

@@ -18,7 +18,7 @@ struct AdamConst {
 // [0, flat_numel).
 struct Walk {
     const Seg *segs;
-    const uint32_t *group;
+    const GroupSeg *group;
     int64_t nseg;
     int64_t ntiles;      // tiles in this launch
     int64_t flat_numel;

@@ -72,10 +72,14 @@ struct ChunkPos {
     int lo, hi;     // the chunk's slots [lo, hi) that belong to the segment
 };
 
-// The segment holding `tile` (a table walk): its group's entry, then the
-// later segments of the group by their first tile.
+// The segment holding `tile` (a table walk): its group's entry, which holds
+// the segment itself unless the tile lies past a later segment's start in
+// the group; then those segments by their first tile.
 __device__ __forceinline__ Seg seg_of(const Walk &wk, int64_t tile) {
-    int64_t si = wk.group[tile / kTileGroup];
+    const GroupSeg g = wk.group[tile / kTileGroup];
+    if (tile < g.next_tile0)
+        return g.seg;
+    int64_t si = g.index + 1;
     Seg cur = wk.segs[si];
     while (si + 1 < wk.nseg) {
         const Seg nxt = wk.segs[si + 1];

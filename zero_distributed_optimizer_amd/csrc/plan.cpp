@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <limits>
 #include <new>
 
 #include "zdo_internal.h"
@@ -165,28 +166,38 @@ int upload_plan(zdo_plan &p) {
         }
         return g;
     };
-    const auto param_group =
-        group_index(p.param_tiles, p.param_segs.size(), [&](size_t s) { return p.param_segs[s].tile0; });
-    const auto range_group =
-        group_index(p.range_tiles, p.range_segs.size(), [&](size_t s) { return p.range_segs[s].tile0; });
+    auto group_segs = [&](const std::vector<Seg> &segs, int64_t ntiles) {
+        const auto idx = group_index(ntiles, segs.size(), [&](size_t s) { return segs[s].tile0; });
+        std::vector<GroupSeg> g(idx.size());
+        for (size_t i = 0; i < idx.size(); ++i) {
+            const size_t s = idx[i];
+            g[i] = {segs[s], int64_t(s),
+                    s + 1 < segs.size() ? segs[s + 1].tile0 : std::numeric_limits<int64_t>::max()};
+        }
+        return g;
+    };
+    const auto param_group = group_segs(p.param_segs, p.param_tiles);
+    const auto range_group = group_segs(p.range_segs, p.range_tiles);
     const auto gather_group =
         group_index(p.gather_tiles, p.gather_ranges.size(), [&](size_t y) { return p.gather_ranges[y].tile0; });
-    // one allocation: segments, gather ranges, then the three group indexes
+    // one allocation: segments, the two walks' group entries, the gather
+    // ranges, then the gather's group index
     const size_t nseg = p.param_segs.size() + p.range_segs.size();
     const size_t seg_bytes = nseg * sizeof(Seg);
+    const size_t gseg_bytes = (param_group.size() + range_group.size()) * sizeof(GroupSeg);
     const size_t span_bytes = p.gather_ranges.size() * sizeof(RangeSpan);
-    const size_t ngroup = param_group.size() + range_group.size() + gather_group.size();
-    const size_t bytes = seg_bytes + span_bytes + ngroup * sizeof(uint32_t);
+    const size_t bytes = seg_bytes + gseg_bytes + span_bytes + gather_group.size() * sizeof(uint32_t);
     std::vector<char> host(bytes);
     std::copy(p.param_segs.begin(), p.param_segs.end(), reinterpret_cast<Seg *>(host.data()));
     std::copy(p.range_segs.begin(), p.range_segs.end(),
               reinterpret_cast<Seg *>(host.data()) + p.param_segs.size());
+    GroupSeg *gs = reinterpret_cast<GroupSeg *>(host.data() + seg_bytes);
+    gs = std::copy(param_group.begin(), param_group.end(), gs);
+    std::copy(range_group.begin(), range_group.end(), gs);
     std::copy(p.gather_ranges.begin(), p.gather_ranges.end(),
-              reinterpret_cast<RangeSpan *>(host.data() + seg_bytes));
-    uint32_t *gi = reinterpret_cast<uint32_t *>(host.data() + seg_bytes + span_bytes);
-    gi = std::copy(param_group.begin(), param_group.end(), gi);
-    gi = std::copy(range_group.begin(), range_group.end(), gi);
-    std::copy(gather_group.begin(), gather_group.end(), gi);
+              reinterpret_cast<RangeSpan *>(host.data() + seg_bytes + gseg_bytes));
+    std::copy(gather_group.begin(), gather_group.end(),
+              reinterpret_cast<uint32_t *>(host.data() + seg_bytes + gseg_bytes + span_bytes));
     void *d = nullptr;
     hipError_t e = hipMalloc(&d, bytes);
     if (e != hipSuccess) {
@@ -203,10 +214,11 @@ int upload_plan(zdo_plan &p) {
     p.d_table = d;
     p.d_param_segs = static_cast<const Seg *>(d);
     p.d_range_segs = p.d_param_segs + p.param_segs.size();
-    p.d_gather_ranges = reinterpret_cast<const RangeSpan *>(static_cast<const char *>(d) + seg_bytes);
-    p.d_param_group = reinterpret_cast<const uint32_t *>(static_cast<const char *>(d) + seg_bytes + span_bytes);
+    p.d_param_group = reinterpret_cast<const GroupSeg *>(static_cast<const char *>(d) + seg_bytes);
     p.d_range_group = p.d_param_group + param_group.size();
-    p.d_gather_group = p.d_range_group + range_group.size();
+    p.d_gather_ranges = reinterpret_cast<const RangeSpan *>(static_cast<const char *>(d) + seg_bytes + gseg_bytes);
+    p.d_gather_group =
+        reinterpret_cast<const uint32_t *>(static_cast<const char *>(d) + seg_bytes + gseg_bytes + span_bytes);
     p.device = dev;
     if (hipDeviceGetAttribute(&p.lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
         hipSuccess) {

@@ -40,8 +40,18 @@ inline int64_t seg_tiles(int64_t wbeg, int64_t len) {
 // Tiles map to their segment (or range) through one entry per kTileGroup
 // tiles: the one holding the group's first tile; the few later ones of the
 // group follow by their tile0. The index stays small enough to live in the
-// L2 cache (4 bytes per 64 tiles), so a tile's lookup does not go to HBM.
+// L2 cache, so a tile's lookup does not go to HBM.
 constexpr int64_t kTileGroup = 64;
+
+// A group entry of the segment walks: a copy of the segment holding the
+// group's first tile, with that segment's index and the next segment's first
+// tile, so that a workgroup finds its segment in one load unless its tile
+// lies past a segment start inside the group.
+struct GroupSeg {
+    Seg seg;
+    int64_t index;
+    int64_t next_tile0;  // first tile of segment index + 1, or INT64_MAX
+};
 
 // One rank range of one padded bucket, as the all-gather walks it: tiles of
 // kGatherTile elements from rb rounded down to kAnchor.
@@ -84,7 +94,7 @@ struct zdo_plan {
     // gather ranges, and the kTileGroup index of each launch space.
     void *d_table = nullptr;
     const zdo::Seg *d_param_segs = nullptr, *d_range_segs = nullptr;
-    const uint32_t *d_param_group = nullptr, *d_range_group = nullptr;
+    const zdo::GroupSeg *d_param_group = nullptr, *d_range_group = nullptr;
     const zdo::RangeSpan *d_gather_ranges = nullptr;
     const uint32_t *d_gather_group = nullptr;
     int device = -1;

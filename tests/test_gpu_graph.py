@@ -1,7 +1,9 @@
 """The launch calls inside a HIP graph: the clipping pipeline (squared norms of
-every rank, the coefficient, every rank's clipped step) and the plain fused
-step are captured once and replayed several times, with eager work between
-replays; every replay must equal the same calls run eagerly. The calls
+every rank, the coefficient, every rank's clipped step), the plain fused
+step, the ZeRO-1 loop (every rank's step, then every rank's all-gather) and
+the one-pass two-instance step are captured once and replayed several times,
+with eager work between replays; every replay must equal the same calls run
+eagerly. The calls
 allocate nothing and never synchronise the host, and no memset is recorded
 (the norm's workspace needs no clearing)."""
 
@@ -73,5 +75,63 @@ def test_graph_replays_equal_eager(gpu, max_norm):
             assert torch.equal(x.view(torch.int32), y.view(torch.int32)), f"replay {replay} fused"
         assert torch.equal(graphed["fused_params"], eager["fused_params"]), f"replay {replay} fused"
         assert torch.equal(graphed["parts"], eager["parts"]) and torch.equal(graphed["coeff"], eager["coeff"])
+    del g
+    free()
+
+
+def _loop(gpu, w, plans, reps, reps2, states, bufs, inst_state, inst_params, hpk):
+    """Every rank's step into its own parameter buffer, then every rank's
+    all-gather in place; and one two-instance step in one pass."""
+    D = w.dp_size
+    for r in range(D):
+        gpu.sharded_adam_step(plans[r], reps, gpu.WORLD, w.scale, *states[r], bufs[r], gpu.WORLD, **hpk)
+    for r in range(D):
+        gpu.all_gather_params(plans[r], bufs, bufs[r])
+    gpu.sharded_adam_step_instances(plans[2], [reps, reps2], gpu.WORLD, w.scale / 2, *inst_state, inst_params,
+                                    gpu.WORLD, **hpk)
+
+
+def test_graph_zero1_loop_and_instances(gpu):
+    w = W.get("tiny")
+    D = w.dp_size
+    N = OL.build_layout(w.param_numel, w.bucket_numel, D).buffer_numel
+    plans = [gpu.build_range_map(w.param_numel, w.bucket_numel, D, r) for r in range(D)]
+    reps = _gen_world(w, N)
+    reps2 = _gen_world(w, N, step=1)
+    hpk = hp_kwargs(w.hp, 2)
+    base = torch.randn(N, device=DEV).mul_(0.02).to(torch.bfloat16).view(torch.int16)
+
+    def fresh():
+        return dict(states=[_gen_state(w, p.shard_numel) for p in plans],
+                    bufs=[base.clone() for _ in range(D)],
+                    inst_state=_gen_state(w, plans[2].shard_numel),
+                    inst_params=torch.full((N,), SENTINEL, dtype=torch.int16, device=DEV))
+
+    eager, graphed = fresh(), fresh()
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            _loop(gpu, w, plans, reps, reps2, graphed["states"], graphed["bufs"], graphed["inst_state"],
+                  graphed["inst_params"], hpk)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    for replay in range(4):
+        g.replay()
+        _loop(gpu, w, plans, reps, reps2, eager["states"], eager["bufs"], eager["inst_state"], eager["inst_params"],
+              hpk)
+        torch.cuda.synchronize()
+        scratch = torch.randn(1 << 20, device=DEV)
+        scratch.mul_(2.0)
+        for a, b in zip(graphed["states"], eager["states"]):
+            for x, y in zip(a, b):
+                assert torch.equal(x.view(torch.int32), y.view(torch.int32)), f"replay {replay}"
+        for r in range(D):
+            assert torch.equal(graphed["bufs"][r], eager["bufs"][r]), f"replay {replay} rank {r}"
+            assert torch.equal(eager["bufs"][r], eager["bufs"][0]), "every rank holds the same parameters"
+        for x, y in zip(graphed["inst_state"], eager["inst_state"]):
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32)), f"replay {replay} instances"
+        assert torch.equal(graphed["inst_params"], eager["inst_params"]), f"replay {replay} instances"
     del g
     free()

@@ -11,8 +11,10 @@
  * the sum over its range (§4.2), copied into the rank's fp32 main-grad
  * shard through the four-way range map (§4.1, §4.3), Adam runs on the fp32
  * master/m/v shard only (§4.3), and the updated parameters are written back
- * as bf16 into the owned range of the parameter buffer (§4.3).
- * force_all_reduce produces the whole reduced buffer instead (§5).
+ * as bf16 into the owned range of the parameter buffer (§4.3); the
+ * all-gather of the parameter buffers then gives every rank the whole
+ * updated parameters (§4.4, all_gather_params). force_all_reduce produces
+ * the whole reduced buffer instead of the reduce-scatter (§5).
  *
  * On one GPU, the D ranks' contributions are D replica buffers in this
  * GPU's memory; the library sums them itself (no collective library).

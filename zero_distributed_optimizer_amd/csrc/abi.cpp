@@ -303,9 +303,9 @@ int force_all_reduce(const zdo_plan *plan, const uint16_t *const *replicas, int3
 // n_instances groups of n_grads / n_instances contributions (1 for the plain
 // step).
 static int adam_step(const char *fn, const zdo_plan *plan, int32_t b0, int32_t b1, const uint16_t *const *grads,
-                     int32_t n_grads, int32_t n_instances, int32_t grad_coords, float scale, float *master, float *exp_avg,
-                     float *exp_avg_sq, uint16_t *param_out, int32_t param_coords, const zdo_adam *hp,
-                     const float *coeff, float *main_grad_out, void *stream) {
+                     int32_t n_grads, int32_t n_instances, int32_t grad_coords, float scale, float *master,
+                     float *exp_avg, float *exp_avg_sq, uint16_t *param_out, int32_t param_coords,
+                     const zdo_adam *hp, const float *coeff, float *main_grad_out, void *stream) {
     if (int rc = check_plan(plan, fn))
         return rc;
     if (b1 < 0)

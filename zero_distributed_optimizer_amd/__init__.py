@@ -116,7 +116,7 @@ def require_library() -> ctypes.CDLL:
     for f in ("build_range_map", "zdo_plan_buckets", "zdo_plan_pieces", "reduce_scatter_local",
               "force_all_reduce", "sharded_adam_step", "writeback_params", "grad_norm_sq", "clip_coefficient",
               "sharded_adam_step_clipped", "reduce_scatter_local_buckets", "sharded_adam_step_buckets",
-              "zdo_device_copy"):
+              "sharded_adam_step_instances", "all_gather_params", "zdo_device_copy"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L

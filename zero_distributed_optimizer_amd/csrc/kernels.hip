@@ -80,17 +80,36 @@ struct ChunkPos {
     int lo, hi;     // the chunk's slots [lo, hi) that belong to the segment
 };
 
+// The plan's tables are read-only for the life of the plan: read through the
+// constant address space, the compiler fetches them with scalar loads (one
+// per wave, into scalar registers) instead of 64-lane vector loads of one
+// address.
+template <typename T>
+using ro_ptr = const __attribute__((address_space(4))) T *;
+template <typename T>
+__device__ __forceinline__ ro_ptr<T> ro(const T *p) {
+    return (ro_ptr<T>)(p);
+}
+__device__ __forceinline__ Seg ld_seg(ro_ptr<Seg> p) {
+    Seg s;
+    s.wbeg = p->wbeg;
+    s.lbeg = p->lbeg;
+    s.len = p->len;
+    s.tile0 = p->tile0;
+    return s;
+}
+
 // The segment holding `tile` (a table walk): its group's entry, which holds
 // the segment itself unless the tile lies past a later segment's start in
 // the group; then those segments by their first tile.
 __device__ __forceinline__ Seg seg_of(const Walk &wk, int64_t tile) {
-    const GroupSeg g = wk.group[tile / kTileGroup];
-    if (tile < g.next_tile0)
-        return g.seg;
-    int64_t si = g.index + 1;
-    Seg cur = wk.segs[si];
+    const ro_ptr<GroupSeg> g = ro(wk.group) + tile / kTileGroup;
+    if (tile < g->next_tile0)
+        return ld_seg(&g->seg);
+    int64_t si = g->index + 1;
+    Seg cur = ld_seg(ro(wk.segs) + si);
     while (si + 1 < wk.nseg) {
-        const Seg nxt = wk.segs[si + 1];
+        const Seg nxt = ld_seg(ro(wk.segs) + si + 1);
         if (nxt.tile0 > tile)
             break;
         cur = nxt;
@@ -597,10 +616,11 @@ constexpr int kGatherChunks = int(kGatherTile / kTileElems);   // chunks per lan
 
 __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a) {
     for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
-        int64_t y = a.group[tile / kTileGroup];
-        while (y + 1 < a.nranges && a.ranges[y + 1].tile0 <= tile)
+        int64_t y = ro(a.group)[tile / kTileGroup];
+        while (y + 1 < a.nranges && ro(a.ranges)[y + 1].tile0 <= tile)
             ++y;
-        const RangeSpan r = a.ranges[y];
+        const ro_ptr<RangeSpan> rp = ro(a.ranges) + y;
+        const RangeSpan r = {rp->rb, rp->re, rp->tile0, rp->src};
         const uint16_t *src = a.src[r.src];
         if (src == a.out)
             continue;

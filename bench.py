@@ -339,6 +339,14 @@ def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> d
     t_step = timed(lambda: zdo.sharded_adam_step_clipped(plan, [red], zdo.LOCAL, 1.0, *st, par, coords,
                                                          grad_coeff=coeff, stream=stream, **hp))
     t_all = t_norm + t_clip + t_step
+    # the step on one pre-reduced gradient, as after a collective
+    # reduce-scatter across devices: 2 + 26 bytes per owned element
+    t_pre = timed(lambda: zdo.sharded_adam_step(plan, [red], zdo.LOCAL, 1.0, *st, par, coords, stream=stream, **hp))
+    out["pre_reduced_step"] = {
+        "path": "sharded_adam_step on one reduced gradient (n_grads = 1, scale 1)", "bytes_per_element": 28,
+        "elements": E, "kernel_avg_us": t_pre * 1e6, "achieved_gbps": E * 28 / t_pre / 1e9,
+        "frac": E * 28 / t_pre / 1e9 / PEAK_HBM_GBPS, "elements_per_s": E / t_pre}
+    log(f"pre-reduced step (n_grads = 1): {t_pre * 1e6:.1f} us, {E * 28 / t_pre / 1e9:.0f} GB/s algorithmic")
     out["clipped_step"] = {
         "path": "grad_norm_sq (writes the reduced gradient) + clip_coefficient + sharded_adam_step_clipped "
                 "(n_grads = 1)",

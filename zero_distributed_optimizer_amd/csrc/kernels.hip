@@ -393,6 +393,8 @@ __device__ __forceinline__ void step_quads(const StepArgs &a, const Quad *q, boo
         mv[h] = ldf4(a.m + q[h].k0);
         vv[h] = ldf4(a.v + q[h].k0);
     }
+    if (clip && cf != cf)
+        return;
     float g[4 * Q];
 #pragma unroll
     for (int k = 0; k < 2 * Q; ++k) {
@@ -430,6 +432,8 @@ __device__ __forceinline__ void step_quads(const StepArgs &a, const Quad *q, boo
 // The step for the slots [lo, hi) of a partial quad, one at a time.
 template <int D, bool kInst>
 __device__ __forceinline__ void step_slots(const StepArgs &a, const Quad &q, bool clip, float cf) {
+    if (clip && cf != cf)
+        return;
     const int64_t gi = a.in_local ? q.k0 : q.w0;
     const int64_t pi = a.param_local ? q.k0 : q.w0;
     for (int e = q.lo; e < q.hi; ++e) {
@@ -456,13 +460,10 @@ template <int D, bool kInst>
 __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a) {
     // Global-norm clipping: the main grad is multiplied by the coefficient; a
     // NaN coefficient (found-inf) leaves everything unchanged.
+    // The coefficient is read alongside the tile's lookup and tested only
+    // before the first store, so its latency overlaps the tile's loads.
     const bool clip = a.coeff != nullptr;
-    float cf = 1.0f;
-    if (clip) {
-        cf = *a.coeff;
-        if (cf != cf)
-            return;
-    }
+    const float cf = clip ? *ro(a.coeff) : 1.0f;
     for (int64_t tile = a.walk.tile_begin + blockIdx.x; tile < a.walk.tile_begin + a.walk.ntiles;
          tile += gridDim.x) {
         Quad q[2];

@@ -393,8 +393,6 @@ __device__ __forceinline__ void step_quads(const StepArgs &a, const Quad *q, boo
         mv[h] = ldf4(a.m + q[h].k0);
         vv[h] = ldf4(a.v + q[h].k0);
     }
-    if (clip && cf != cf)
-        return;
     float g[4 * Q];
 #pragma unroll
     for (int k = 0; k < 2 * Q; ++k) {
@@ -432,8 +430,6 @@ __device__ __forceinline__ void step_quads(const StepArgs &a, const Quad *q, boo
 // The step for the slots [lo, hi) of a partial quad, one at a time.
 template <int D, bool kInst>
 __device__ __forceinline__ void step_slots(const StepArgs &a, const Quad &q, bool clip, float cf) {
-    if (clip && cf != cf)
-        return;
     const int64_t gi = a.in_local ? q.k0 : q.w0;
     const int64_t pi = a.param_local ? q.k0 : q.w0;
     for (int e = q.lo; e < q.hi; ++e) {
@@ -460,12 +456,13 @@ template <int D, bool kInst>
 __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a) {
     // Global-norm clipping: the main grad is multiplied by the coefficient; a
     // NaN coefficient (found-inf) leaves everything unchanged.
-    // The coefficient is read alongside the tile's lookup and tested only
-    // before the first store, so its latency overlaps the tile's loads.
+    // The coefficient load goes out with the walk's arguments, and a NaN
+    // empties the tile range instead of branching: a test inside the tile
+    // body would split the block that issues all of a tile's loads at once.
     const bool clip = a.coeff != nullptr;
     const float cf = clip ? *ro(a.coeff) : 1.0f;
-    for (int64_t tile = a.walk.tile_begin + blockIdx.x; tile < a.walk.tile_begin + a.walk.ntiles;
-         tile += gridDim.x) {
+    const int64_t tend = clip && cf != cf ? a.walk.tile_begin : a.walk.tile_begin + a.walk.ntiles;
+    for (int64_t tile = a.walk.tile_begin + blockIdx.x; tile < tend; tile += gridDim.x) {
         Quad q[2];
         quads_of(a.walk, tile, q);
         if (full(q[0]) && full(q[1])) {

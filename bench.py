@@ -11,7 +11,8 @@ bf16 replica buffers in HBM.
 Prints one JSON line: elements/s of the step (wall clock over the timed
 steps), the HBM roofline of the step kernel (algorithmic bytes (2D+26) per
 owned element over its average duration, from HIP events on the launch
-stream), and the CPU oracle timed on a bounded sample beside it.
+stream: one event pair around the timed steps, so that the average is the
+region over K), and the CPU oracle timed on a bounded sample beside it.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--rank R]
 """
@@ -137,26 +138,45 @@ def main() -> int:
         step(t)
     torch.cuda.synchronize(dev)
 
-    # timed region: K back-to-back steps, a HIP event pair around every launch
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # timed region: K back-to-back steps between one HIP event pair on the
+    # launch stream; the average launch duration is the region over K. An
+    # event pair around every launch would drain the queue before and after
+    # each step and slow the steps it measures (GPT-2 shape: 96.8 us per step
+    # back to back, 98.7-99.6 us per step between per-launch pairs)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize(dev)
     w0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
         t += 1
-        ev[i][0].record(stream)
         step(t)
-        ev[i][1].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - w0
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
     ms_per_step = wall * 1e3 / args.steps
-    kern_avg_s = float(np.mean(kern_ms)) / 1e3
+    kern_avg_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
     bytes_per_elem = 2 * D + 26
     alg_bytes = E * bytes_per_elem
     achieved = alg_bytes / kern_avg_s / 1e9
-    log(f"step: wall {ms_per_step * 1e3:.1f} us/step, kernel avg {kern_avg_s * 1e6:.1f} us "
-        f"(p10 {np.percentile(kern_ms, 10) * 1e3:.1f}, p90 {np.percentile(kern_ms, 90) * 1e3:.1f}), "
+    log(f"step: wall {ms_per_step * 1e3:.1f} us/step, kernel avg {kern_avg_s * 1e6:.1f} us, "
         f"{achieved:.0f} GB/s algorithmic")
+
+    # after the timed region: single launches between their own event pairs,
+    # for the spread of one launch's duration
+    n_iso = min(args.steps, 50)
+    iev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_iso)]
+    for a, b in iev:
+        t += 1
+        a.record(stream)
+        step(t)
+        b.record(stream)
+    torch.cuda.synchronize(dev)
+    iso_ms = [a.elapsed_time(b) for a, b in iev]
+    isolated = {"steps": n_iso, "avg_us": float(np.mean(iso_ms)) * 1e3,
+                "p10_us": float(np.percentile(iso_ms, 10)) * 1e3, "p90_us": float(np.percentile(iso_ms, 90)) * 1e3,
+                "how": "each launch between its own event pair, after the timed region"}
+    log(f"single launches: avg {isolated['avg_us']:.1f} us (p10 {isolated['p10_us']:.1f}, "
+        f"p90 {isolated['p90_us']:.1f})")
 
     # plain-copy reference on the same stream (1 GiB read + 1 GiB write)
     nb = 1 << 30
@@ -164,13 +184,13 @@ def main() -> int:
     dst = torch.empty_like(src)
     for _ in range(3):
         zdo.device_copy(dst, src, stream)
-    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
-    for a, b in cev:
-        a.record(stream)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
         zdo.device_copy(dst, src, stream)
-        b.record(stream)
+    c1.record(stream)
     torch.cuda.synchronize(dev)
-    copy_gbps = 2 * nb / (float(np.mean([a.elapsed_time(b) for a, b in cev])) / 1e3) / 1e9
+    copy_gbps = 2 * nb / (c0.elapsed_time(c1) / 1e3 / 10) / 1e9
     log(f"copy reference: {copy_gbps:.0f} GB/s")
 
     # cold caches: the same step after 1 GiB of ordinary (temporal) reads,
@@ -241,8 +261,8 @@ def main() -> int:
             "traffic": traffic,
         },
         "kernel": {"name": "step_kernel", "avg_us": kern_avg_s * 1e6,
-                   "p10_us": float(np.percentile(kern_ms, 10)) * 1e3,
-                   "p90_us": float(np.percentile(kern_ms, 90)) * 1e3,
+                   "how": "one HIP event pair around the timed steps on the launch stream, divided by the steps",
+                   "single_launches": isolated,
                    "source_sha256_16": kernel_source_hash()},
         "cold_cache": cold,
         "variants": variants,
@@ -261,22 +281,24 @@ def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> d
     pass), the parameter all-gather in place (4 bytes per element of the
     other ranks' ranges) and, when the replicas are whole buffers,
     force_all_reduce over the padded buffer (2D + 2 bytes per buffer
-    element). HIP events around each launch."""
+    element). Each call timed as n back-to-back calls between one HIP event
+    pair."""
     import workloads as W
 
     D = plan.dp_size
     out = {}
 
     def timed(fn) -> float:
+        """Average seconds per call of n back-to-back calls between one event pair."""
         for _ in range(3):
             fn()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        for a, b in ev:
-            a.record(stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
             fn()
-            b.record(stream)
+        b.record(stream)
         torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+        return a.elapsed_time(b) / 1e3 / n
 
     ranges = int(sum(b["shard_numel"] for b in plan.buckets()))
     red = torch.empty(plan.shard_numel, dtype=torch.int16, device=reps[0].device)

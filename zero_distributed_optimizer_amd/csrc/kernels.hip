@@ -377,15 +377,15 @@ __device__ __forceinline__ void reduce_quads(const StepArgs &a, const int64_t *g
     }
 }
 
-// The whole step for Q full quads: reduce, Adam, write-back.
+// The whole step for Q full quads: reduce, Adam, write-back. The state loads
+// come first, so that they are in flight together with the contributions'
+// loads rather than after the reduction.
 template <int D, bool kInst, int Q>
 __device__ __forceinline__ void step_quads(const StepArgs &a, const Quad *q, bool clip, float cf) {
     int64_t gi[Q];
 #pragma unroll
     for (int h = 0; h < Q; ++h)
         gi[h] = a.in_local ? q[h].k0 : q[h].w0;
-    float acc[4 * Q];
-    reduce_quads<D, kInst, Q>(a, gi, acc);
     f32x4 pv[Q], mv[Q], vv[Q];
 #pragma unroll
     for (int h = 0; h < Q; ++h) {
@@ -393,6 +393,8 @@ __device__ __forceinline__ void step_quads(const StepArgs &a, const Quad *q, boo
         mv[h] = ldf4(a.m + q[h].k0);
         vv[h] = ldf4(a.v + q[h].k0);
     }
+    float acc[4 * Q];
+    reduce_quads<D, kInst, Q>(a, gi, acc);
     float g[4 * Q];
 #pragma unroll
     for (int k = 0; k < 2 * Q; ++k) {
@@ -452,8 +454,14 @@ __device__ __forceinline__ void step_slots(const StepArgs &a, const Quad &q, boo
 
 // kInst: a.rep holds a.ninst instances of D (or, for D = 0, a.dinst)
 // contributions each; otherwise a.nrep contributions of one instance.
+//
+// The occupancy bounds tell the compiler how many waves can share a SIMD,
+// which the launches cap anyway (lds_reserve): with at most 4 (3 for 32
+// contributions, 166 registers), it keeps every load of a tile in flight
+// before the first wait instead of interleaving waits to save registers.
 template <int D, bool kInst>
-__global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(D >= 32 && !kInst ? 3 : 1, D < 32 ? 4 : 3)))
+void step_kernel(StepArgs a) {
     // Global-norm clipping: the main grad is multiplied by the coefficient; a
     // NaN coefficient (found-inf) leaves everything unchanged.
     // The coefficient load goes out with the walk's arguments, and a NaN
@@ -665,19 +673,25 @@ unsigned grid_for(int64_t ntiles) {
 // rounds of workgroups over the chip, finishes sooner with more waves in
 // flight (GPT-2-shaped step, 30k tiles: 106 us at 10 waves per compute unit,
 // 102 us at 16; its clipped step 92 us at 10, 78 us at 16). The launch
-// reserves LDS it never uses so that at most ZDO_WAVES_PER_CU waves, or
-// ZDO_WAVES_PER_CU_SHORT for launches of fewer than kShortLaunchTiles tiles,
-// fit on one compute unit.
+// reserves LDS it never uses so that at most `long_waves` waves (by default
+// ZDO_WAVES_PER_CU), or ZDO_WAVES_PER_CU_SHORT for launches of fewer than
+// kShortLaunchTiles tiles, fit on one compute unit. A step with a fixed
+// number (2 to 32) of contributions has every load of a tile in flight at
+// once and needs fewer waves to cover the latency: its long launches take
+// ZDO_STEP_WAVES_PER_CU.
 #ifndef ZDO_WAVES_PER_CU
 #define ZDO_WAVES_PER_CU 10
 #endif
 #ifndef ZDO_WAVES_PER_CU_SHORT
 #define ZDO_WAVES_PER_CU_SHORT 16
 #endif
+#ifndef ZDO_STEP_WAVES_PER_CU
+#define ZDO_STEP_WAVES_PER_CU 6
+#endif
 constexpr int64_t kShortLaunchTiles = int64_t(1) << 17;
 
-unsigned lds_reserve(int lds_per_cu, int64_t ntiles) {
-    const int waves = ntiles < kShortLaunchTiles ? ZDO_WAVES_PER_CU_SHORT : ZDO_WAVES_PER_CU;
+unsigned lds_reserve(int lds_per_cu, int64_t ntiles, int long_waves = ZDO_WAVES_PER_CU) {
+    const int waves = ntiles < kShortLaunchTiles ? ZDO_WAVES_PER_CU_SHORT : long_waves;
     if (waves <= 0 || lds_per_cu <= 0)
         return 0;
     const int waves_per_group = kBlock / 64;
@@ -710,7 +724,9 @@ hipError_t launch_step(const StepArgs &a, int lds_per_cu, hipStream_t stream) {
     if (a.walk.ntiles <= 0)
         return hipSuccess;
     const dim3 grid(grid_for(a.walk.ntiles)), block(kBlock);
-    const unsigned lds = lds_reserve(lds_per_cu, a.walk.ntiles);
+    const int d = a.ninst > 1 && a.dinst > 1 ? a.dinst : a.nrep;   // the template's D
+    const bool fixed = d == 2 || d == 4 || d == 8 || d == 16 || d == 32;
+    const unsigned lds = lds_reserve(lds_per_cu, a.walk.ntiles, fixed ? ZDO_STEP_WAVES_PER_CU : ZDO_WAVES_PER_CU);
     // One contribution per instance is the plain sum over the instances: the
     // inner rounding of a single bf16 term changes nothing.
     if (a.ninst > 1 && a.dinst > 1) {

@@ -385,6 +385,7 @@ static int adam_step(const char *fn, const zdo_plan *plan, int32_t b0, int32_t b
     a.param = param_out;
     a.main_grad = main_grad_out;
     a.coeff = coeff;
+    a.state_numel = L;
     a.c.lr = hp->lr;
     a.c.b1 = hp->beta1;
     a.c.b2 = hp->beta2;

@@ -51,6 +51,7 @@ struct StepArgs {
     uint16_t *param;     // may be NULL
     float *main_grad;    // may be NULL
     const float *coeff;  // device clipping coefficient, or NULL for none
+    int64_t state_numel; // L: the master/m/v arrays' length (selects their cache policy)
     AdamConst c;
 };
 

@@ -59,8 +59,13 @@ __device__ __forceinline__ uint32_t to_bf16x2(float a, float b) {
 // reduced gradient, main grad) are non-temporal stores too (Llama-3-8B-shaped
 // step: 6.83 ms in every run against 6.83-7.48 ms with plain stores;
 // Llama-3-70B-shaped reduce-scatter 7% faster). The fp32 state is read and
-// then rewritten: plain loads and stores (non-temporal ones measured slower
-// there).
+// then rewritten. When it fits the 256 MB Infinity Cache, plain loads and
+// stores let the next step find it there (GPT-2-shaped step, 187 MB of
+// state, back to back: 97.5 us against 109.8 us with non-temporal state
+// accesses). When it does not, the step loads and stores it non-temporally
+// as well (Llama-3-8B-shaped step: 6.92-6.98 -> 6.75-6.77 ms); non-temporal
+// stores after plain loads of the same lines are far slower than either
+// (3.4-3.6 TB/s).
 __device__ __forceinline__ u32x4 ld_rep(const uint16_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
@@ -71,6 +76,20 @@ __device__ __forceinline__ void st16_out(uint16_t *p, u32x4 v) {
 __device__ __forceinline__ void stf4(float *p, f32x4 v) { *reinterpret_cast<f32x4 *>(p) = v; }
 __device__ __forceinline__ void stf4_out(float *p, f32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
+}
+template <bool kNT>
+__device__ __forceinline__ f32x4 ld_state(const float *p) {
+    if constexpr (kNT)
+        return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+    else
+        return ldf4(p);
+}
+template <bool kNT>
+__device__ __forceinline__ void st_state(float *p, f32x4 v) {
+    if constexpr (kNT)
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
+    else
+        stf4(p, v);
 }
 
 // ---- walking the segments -------------------------------------------------------------
@@ -380,7 +399,7 @@ __device__ __forceinline__ void reduce_quads(const StepArgs &a, const int64_t *g
 // The whole step for Q full quads: reduce, Adam, write-back. The state loads
 // come first, so that they are in flight together with the contributions'
 // loads rather than after the reduction.
-template <int D, bool kInst, int Q>
+template <int D, bool kInst, int Q, bool kNT>
 __device__ __forceinline__ void step_quads(const StepArgs &a, const Quad *q, bool clip, float cf) {
     int64_t gi[Q];
 #pragma unroll
@@ -389,9 +408,9 @@ __device__ __forceinline__ void step_quads(const StepArgs &a, const Quad *q, boo
     f32x4 pv[Q], mv[Q], vv[Q];
 #pragma unroll
     for (int h = 0; h < Q; ++h) {
-        pv[h] = ldf4(a.master + q[h].k0);
-        mv[h] = ldf4(a.m + q[h].k0);
-        vv[h] = ldf4(a.v + q[h].k0);
+        pv[h] = ld_state<kNT>(a.master + q[h].k0);
+        mv[h] = ld_state<kNT>(a.m + q[h].k0);
+        vv[h] = ld_state<kNT>(a.v + q[h].k0);
     }
     float acc[4 * Q];
     reduce_quads<D, kInst, Q>(a, gi, acc);
@@ -418,9 +437,9 @@ __device__ __forceinline__ void step_quads(const StepArgs &a, const Quad *q, boo
             adam(a.c, g[4 * h + e], p[e], m[e], v[e]);
         }
         const int64_t k0 = q[h].k0;
-        stf4(a.master + k0, f32x4{p[0], p[1], p[2], p[3]});
-        stf4(a.m + k0, f32x4{m[0], m[1], m[2], m[3]});
-        stf4(a.v + k0, f32x4{v[0], v[1], v[2], v[3]});
+        st_state<kNT>(a.master + k0, f32x4{p[0], p[1], p[2], p[3]});
+        st_state<kNT>(a.m + k0, f32x4{m[0], m[1], m[2], m[3]});
+        st_state<kNT>(a.v + k0, f32x4{v[0], v[1], v[2], v[3]});
         if (a.main_grad)
             stf4_out(a.main_grad + k0, f32x4{g[4 * h], g[4 * h + 1], g[4 * h + 2], g[4 * h + 3]});
         if (a.param)
@@ -455,11 +474,14 @@ __device__ __forceinline__ void step_slots(const StepArgs &a, const Quad &q, boo
 // kInst: a.rep holds a.ninst instances of D (or, for D = 0, a.dinst)
 // contributions each; otherwise a.nrep contributions of one instance.
 //
+// kNT: the fp32 state is loaded and stored non-temporally (it does not fit
+// the Infinity Cache; see the memory helpers above).
+//
 // The occupancy bounds tell the compiler how many waves can share a SIMD,
 // which the launches cap anyway (lds_reserve): with at most 4 (3 for 32
 // contributions, 166 registers), it keeps every load of a tile in flight
 // before the first wait instead of interleaving waits to save registers.
-template <int D, bool kInst>
+template <int D, bool kInst, bool kNT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(D >= 32 && !kInst ? 3 : 1, D < 32 ? 4 : 3)))
 void step_kernel(StepArgs a) {
     // Global-norm clipping: the main grad is multiplied by the coefficient; a
@@ -474,12 +496,12 @@ void step_kernel(StepArgs a) {
         Quad q[2];
         quads_of(a.walk, tile, q);
         if (full(q[0]) && full(q[1])) {
-            step_quads<D, kInst, 2>(a, q, clip, cf);
+            step_quads<D, kInst, 2, kNT>(a, q, clip, cf);
         } else {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 if (full(q[h]))
-                    step_quads<D, kInst, 1>(a, q + h, clip, cf);
+                    step_quads<D, kInst, 1, kNT>(a, q + h, clip, cf);
                 else
                     step_slots<D, kInst>(a, q[h], clip, cf);
             }
@@ -720,6 +742,38 @@ hipError_t launch_reduce(const ReduceArgs &a, int lds_per_cu, hipStream_t stream
     return hipGetLastError();
 }
 
+// The fp32 state goes non-temporal when it cannot stay in the Infinity
+// Cache between steps.
+#ifndef ZDO_STATE_CACHE_BYTES
+#define ZDO_STATE_CACHE_BYTES (int64_t(256) << 20)
+#endif
+
+template <bool kNT>
+void launch_step_as(const StepArgs &a, dim3 grid, dim3 block, unsigned lds, hipStream_t stream) {
+    // One contribution per instance is the plain sum over the instances: the
+    // inner rounding of a single bf16 term changes nothing.
+    if (a.ninst > 1 && a.dinst > 1) {
+        switch (a.dinst) {
+        case 2: hipLaunchKernelGGL((step_kernel<2, true, kNT>), grid, block, lds, stream, a); break;
+        case 4: hipLaunchKernelGGL((step_kernel<4, true, kNT>), grid, block, lds, stream, a); break;
+        case 8: hipLaunchKernelGGL((step_kernel<8, true, kNT>), grid, block, lds, stream, a); break;
+        case 16: hipLaunchKernelGGL((step_kernel<16, true, kNT>), grid, block, lds, stream, a); break;
+        case 32: hipLaunchKernelGGL((step_kernel<32, true, kNT>), grid, block, lds, stream, a); break;
+        default: hipLaunchKernelGGL((step_kernel<0, true, kNT>), grid, block, lds, stream, a); break;
+        }
+        return;
+    }
+    switch (a.nrep) {
+    case 1: hipLaunchKernelGGL((step_kernel<1, false, kNT>), grid, block, lds, stream, a); break;
+    case 2: hipLaunchKernelGGL((step_kernel<2, false, kNT>), grid, block, lds, stream, a); break;
+    case 4: hipLaunchKernelGGL((step_kernel<4, false, kNT>), grid, block, lds, stream, a); break;
+    case 8: hipLaunchKernelGGL((step_kernel<8, false, kNT>), grid, block, lds, stream, a); break;
+    case 16: hipLaunchKernelGGL((step_kernel<16, false, kNT>), grid, block, lds, stream, a); break;
+    case 32: hipLaunchKernelGGL((step_kernel<32, false, kNT>), grid, block, lds, stream, a); break;
+    default: hipLaunchKernelGGL((step_kernel<0, false, kNT>), grid, block, lds, stream, a); break;
+    }
+}
+
 hipError_t launch_step(const StepArgs &a, int lds_per_cu, hipStream_t stream) {
     if (a.walk.ntiles <= 0)
         return hipSuccess;
@@ -727,28 +781,10 @@ hipError_t launch_step(const StepArgs &a, int lds_per_cu, hipStream_t stream) {
     const int d = a.ninst > 1 && a.dinst > 1 ? a.dinst : a.nrep;   // the template's D
     const bool fixed = d == 2 || d == 4 || d == 8 || d == 16 || d == 32;
     const unsigned lds = lds_reserve(lds_per_cu, a.walk.ntiles, fixed ? ZDO_STEP_WAVES_PER_CU : ZDO_WAVES_PER_CU);
-    // One contribution per instance is the plain sum over the instances: the
-    // inner rounding of a single bf16 term changes nothing.
-    if (a.ninst > 1 && a.dinst > 1) {
-        switch (a.dinst) {
-        case 2: hipLaunchKernelGGL((step_kernel<2, true>), grid, block, lds, stream, a); break;
-        case 4: hipLaunchKernelGGL((step_kernel<4, true>), grid, block, lds, stream, a); break;
-        case 8: hipLaunchKernelGGL((step_kernel<8, true>), grid, block, lds, stream, a); break;
-        case 16: hipLaunchKernelGGL((step_kernel<16, true>), grid, block, lds, stream, a); break;
-        case 32: hipLaunchKernelGGL((step_kernel<32, true>), grid, block, lds, stream, a); break;
-        default: hipLaunchKernelGGL((step_kernel<0, true>), grid, block, lds, stream, a); break;
-        }
-        return hipGetLastError();
-    }
-    switch (a.nrep) {
-    case 1: hipLaunchKernelGGL((step_kernel<1, false>), grid, block, lds, stream, a); break;
-    case 2: hipLaunchKernelGGL((step_kernel<2, false>), grid, block, lds, stream, a); break;
-    case 4: hipLaunchKernelGGL((step_kernel<4, false>), grid, block, lds, stream, a); break;
-    case 8: hipLaunchKernelGGL((step_kernel<8, false>), grid, block, lds, stream, a); break;
-    case 16: hipLaunchKernelGGL((step_kernel<16, false>), grid, block, lds, stream, a); break;
-    case 32: hipLaunchKernelGGL((step_kernel<32, false>), grid, block, lds, stream, a); break;
-    default: hipLaunchKernelGGL((step_kernel<0, false>), grid, block, lds, stream, a); break;
-    }
+    if (a.state_numel * int64_t(3 * sizeof(float)) > ZDO_STATE_CACHE_BYTES)
+        launch_step_as<true>(a, grid, block, lds, stream);
+    else
+        launch_step_as<false>(a, grid, block, lds, stream);
     return hipGetLastError();
 }
 

@@ -710,6 +710,11 @@ unsigned grid_for(int64_t ntiles) {
 #ifndef ZDO_STEP_WAVES_PER_CU
 #define ZDO_STEP_WAVES_PER_CU 6
 #endif
+// force_all_reduce walks the whole buffer flat. Its long launches do best
+// with 8 waves per compute unit at 8 contributions (GPT-2-shaped buffer:
+// 344-345 us at 10, 335-338 at 8, 358-362 at 7) and with 7 at 16
+// (fragmentation workload: 414-415 us at 10, 413-414 at 8, 394-395 at 7).
+constexpr int flat_waves(int nrep) { return nrep >= 16 ? 7 : 8; }
 constexpr int64_t kShortLaunchTiles = int64_t(1) << 17;
 
 unsigned lds_reserve(int lds_per_cu, int64_t ntiles, int long_waves = ZDO_WAVES_PER_CU) {
@@ -729,7 +734,8 @@ hipError_t launch_reduce(const ReduceArgs &a, int lds_per_cu, hipStream_t stream
     if (a.walk.ntiles <= 0)
         return hipSuccess;
     const dim3 grid(grid_for(a.walk.ntiles)), block(kBlock);
-    const unsigned lds = lds_reserve(lds_per_cu, a.walk.ntiles);
+    const unsigned lds =
+        lds_reserve(lds_per_cu, a.walk.ntiles, a.walk.segs ? ZDO_WAVES_PER_CU : flat_waves(a.nrep));
     switch (a.nrep) {
     case 1: hipLaunchKernelGGL(reduce_kernel<1>, grid, block, lds, stream, a); break;
     case 2: hipLaunchKernelGGL(reduce_kernel<2>, grid, block, lds, stream, a); break;

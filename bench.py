@@ -315,10 +315,12 @@ def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> d
     par_b = torch.empty(plan.extent(coords), dtype=torch.int16, device=reps[0].device)
     hp_b = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, step=1)
 
+    reps_b = zdo.Buffers(reps, "replicas")   # checked once for the nb launches
+
     def per_bucket(st=stream):
         for b in reversed(range(nb)):
-            zdo.sharded_adam_step(plan, reps, coords, w.scale, *st_b, par_b, coords, stream=st, buckets=(b, b + 1),
-                                  **hp_b)
+            zdo.sharded_adam_step(plan, reps_b, coords, w.scale, *st_b, par_b, coords, stream=st,
+                                  buckets=(b, b + 1), **hp_b)
     t_b = timed(per_bucket)
     # the same launches replayed from a HIP graph, so that the host's
     # per-launch cost (Python here) does not leave the GPU idle between
@@ -341,7 +343,7 @@ def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> d
                                            "graph_*: the same launches replayed from a captured HIP graph"}
     log(f"bucket by bucket ({nb} launches): {t_b * 1e6:.1f} us, {gbps:.0f} GB/s algorithmic; "
         f"from a HIP graph {t_g * 1e6:.1f} us")
-    del graph, st_b, par_b
+    del graph, st_b, par_b, reps_b
 
     # global-norm clipping: the rank's squared norm (writing the reduced
     # gradient), the coefficient, the clipped step from the reduced gradient

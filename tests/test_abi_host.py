@@ -150,3 +150,15 @@ def test_plan_accessors_on_null():
     n = ctypes.c_int64()
     assert L.zdo_plan_pieces(None, None, 0, ctypes.byref(n)) == Z.EINVAL
     L.zdo_plan_destroy(None)
+
+
+def test_buffers_reject_host_tensors_and_wrong_dtypes():
+    """zdo.Buffers checks its tensors once, as every call checks a list."""
+    import torch
+    import zero_distributed_optimizer_amd as zdo
+    with pytest.raises(ValueError, match="device"):
+        zdo.Buffers([torch.zeros(8, dtype=torch.int16)], "replicas")
+    with pytest.raises(TypeError, match="torch tensor"):
+        zdo.Buffers([np.zeros(8, np.int16)], "replicas")
+    empty = zdo.Buffers([], "replicas")
+    assert len(empty) == 0 and empty.numel == 0

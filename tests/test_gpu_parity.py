@@ -460,6 +460,37 @@ def test_state_beyond_the_infinity_cache(gpu):
     free()
 
 
+def test_buffers_object_equals_tensor_lists(gpu):
+    """zdo.Buffers (checked once, reused) gives the same bytes as lists of
+    tensors, per bucket and whole; a too-short buffer set is refused."""
+    rng = np.random.default_rng(11)
+    sizes, bucket, D = [700, 5, 1300, 64, 999], 1500, 4
+    lay = OL.build_layout(sizes, bucket, D)
+    N = lay.buffer_numel
+    reps = [to_dev(bf16_host(rng, N)) for _ in range(D)]
+    plan = gpu.build_range_map(sizes, bucket, D, 2)
+    Ln = plan.shard_numel
+    st0 = [(rng.standard_normal(Ln) * 0.02).astype(np.float32) for _ in range(2)] + \
+          [((rng.standard_normal(Ln) * 1e-3) ** 2).astype(np.float32)]
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=3)
+    results = []
+    for use_buffers in (False, True):
+        g = gpu.Buffers(reps, "replicas") if use_buffers else reps
+        st = [to_dev(x) for x in st0]
+        par = torch.full((N,), SENTINEL, dtype=torch.int16, device=DEV)
+        for b in reversed(range(plan.buckets().size)):
+            gpu.sharded_adam_step(plan, g, gpu.WORLD, 0.25, *st, par, gpu.WORLD, buckets=(b, b + 1), **hp)
+        red = torch.full((N,), SENTINEL, dtype=torch.int16, device=DEV)
+        gpu.reduce_scatter_local(plan, g, gpu.WORLD, 0.25, red, gpu.WORLD)
+        results.append([host_f32(x) for x in st] + [host_u16(par), host_u16(red)])
+    for a, b in zip(*results):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    short = gpu.Buffers([r[: N - 1] for r in reps], "replicas")
+    with pytest.raises(ValueError, match="elements per buffer"):
+        gpu.reduce_scatter_local(plan, short, gpu.WORLD, 0.25, red, gpu.WORLD)
+    free()
+
+
 def _sample_slots(plan, rng, n):
     """Owned LOCAL slots: random ones plus the first and last 16 of every piece."""
     pcs = plan.pieces()

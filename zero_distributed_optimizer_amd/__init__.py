@@ -199,7 +199,7 @@ def _dev_ptr(t, what: str, kind: str, numel: int | None) -> int:
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{what}: expected a torch tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{what}: must be a device (cuda) tensor")
     ok = {"bf16": (torch.bfloat16, torch.int16, torch.uint16), "f32": (torch.float32,),
           "f64": (torch.float64,), "bytes": (torch.uint8, torch.int8)}[kind]
@@ -212,7 +212,35 @@ def _dev_ptr(t, what: str, kind: str, numel: int | None) -> int:
     return t.data_ptr()
 
 
+class Buffers:
+    """bf16 device buffers (the D contributions, or the ranks' parameter
+    buffers) checked and marshalled once, for calls repeated on the same
+    tensors: pass it wherever a call takes a list of them. Checking D
+    tensors costs a few microseconds of Python each; a bucket-by-bucket step
+    pays that on every launch otherwise. It holds references to the tensors,
+    which must keep their storage (no resize) while it is in use."""
+
+    def __init__(self, tensors, what: str = "buffers"):
+        self.tensors = tuple(tensors)
+        self.array = (ctypes.c_void_p * len(self.tensors))(
+            *[_dev_ptr(t, f"{what}[{j}]", "bf16", None) for j, t in enumerate(self.tensors)])
+        self.numel = min((int(t.numel()) for t in self.tensors), default=0)
+
+    def __len__(self) -> int:
+        return len(self.tensors)
+
+    def __iter__(self):
+        return iter(self.tensors)
+
+    def __getitem__(self, j):
+        return self.tensors[j]
+
+
 def _ptr_list(ts, what: str, numel: int):
+    if isinstance(ts, Buffers):
+        if ts.numel < numel:
+            raise ValueError(f"{what}: needs at least {numel} elements per buffer, has {ts.numel}")
+        return ts.array
     arr = (ctypes.c_void_p * len(ts))()
     for j, t in enumerate(ts):
         arr[j] = _dev_ptr(t, f"{what}[{j}]", "bf16", numel)

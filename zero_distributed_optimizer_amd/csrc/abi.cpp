@@ -562,7 +562,7 @@ int all_gather_params(const zdo_plan *plan, const uint16_t *const *params, int32
     a.nranges = int64_t(plan->gather_ranges.size());
     a.ntiles = plan->gather_tiles;
     a.out = out;
-    return launch_result(launch_gather(a, static_cast<hipStream_t>(stream)), fn);
+    return launch_result(launch_gather(a, plan->lds_per_cu, static_cast<hipStream_t>(stream)), fn);
 }
 
 int zdo_device_copy(void *dst, const void *src, int64_t bytes, void *stream) {

@@ -91,7 +91,7 @@ hipError_t launch_reduce(const ReduceArgs &a, int lds_per_cu, hipStream_t stream
 hipError_t launch_step(const StepArgs &a, int lds_per_cu, hipStream_t stream);
 hipError_t launch_writeback(const WritebackArgs &a, int lds_per_cu, hipStream_t stream);
 hipError_t launch_copy(void *dst, const void *src, int64_t n16, hipStream_t stream);
-hipError_t launch_gather(const GatherArgs &a, hipStream_t stream);
+hipError_t launch_gather(const GatherArgs &a, int lds_per_cu, hipStream_t stream);
 // Squared norm: per-tile partials into a.partial, then their fixed-order sum
 // into *norm_sq (0 when a.walk has no tiles).
 hipError_t launch_norm(const NormArgs &a, double *norm_sq, int lds_per_cu, hipStream_t stream);

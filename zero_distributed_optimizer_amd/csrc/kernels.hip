@@ -717,8 +717,8 @@ unsigned grid_for(int64_t ntiles) {
 constexpr int flat_waves(int nrep) { return nrep >= 16 ? 7 : 8; }
 constexpr int64_t kShortLaunchTiles = int64_t(1) << 17;
 
-unsigned lds_reserve(int lds_per_cu, int64_t ntiles, int long_waves = ZDO_WAVES_PER_CU) {
-    const int waves = ntiles < kShortLaunchTiles ? ZDO_WAVES_PER_CU_SHORT : long_waves;
+// LDS per workgroup that lets at most `waves` waves share a compute unit.
+unsigned lds_for_waves(int lds_per_cu, int waves) {
     if (waves <= 0 || lds_per_cu <= 0)
         return 0;
     const int waves_per_group = kBlock / 64;
@@ -727,6 +727,17 @@ unsigned lds_reserve(int lds_per_cu, int64_t ntiles, int long_waves = ZDO_WAVES_
         groups = 4 / waves_per_group + (waves_per_group > 4);
     return unsigned(lds_per_cu / groups) & ~127u;
 }
+
+unsigned lds_reserve(int lds_per_cu, int64_t ntiles, int long_waves = ZDO_WAVES_PER_CU) {
+    return lds_for_waves(lds_per_cu, ntiles < kShortLaunchTiles ? ZDO_WAVES_PER_CU_SHORT : long_waves);
+}
+
+// The all-gather's tiles read 4 KiB each. With at most 12 waves per compute
+// unit, short launches and long ones alike ran as fast as uncapped or
+// faster (fragmentation workload 51.3-51.6 -> 49.1-49.8 us, Llama-3-8B
+// shape 4.56-4.62 -> 4.45-4.47 ms, GPT-2 shape 70.1-70.6 -> 70.3-70.5 us;
+// 8 waves: 5-10% slower, 16 and 24: between the two).
+constexpr int kGatherWaves = 12;
 
 }  // namespace
 
@@ -839,12 +850,11 @@ hipError_t launch_clip(const double *parts, int32_t n, float max_norm, float *co
     return hipGetLastError();
 }
 
-hipError_t launch_gather(const GatherArgs &a, hipStream_t stream) {
+hipError_t launch_gather(const GatherArgs &a, int lds_per_cu, hipStream_t stream) {
     if (a.ntiles <= 0)
         return hipSuccess;
-    // 4 KiB read per tile, against 10-40 KiB in the step: no occupancy cap
-    // (as the copy), so that enough bytes are in flight
-    hipLaunchKernelGGL(gather_kernel, dim3(grid_for(a.ntiles)), dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL(gather_kernel, dim3(grid_for(a.ntiles)), dim3(kBlock), lds_for_waves(lds_per_cu, kGatherWaves),
+                       stream, a);
     return hipGetLastError();
 }
 

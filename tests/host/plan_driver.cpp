@@ -16,7 +16,7 @@ hipError_t launch_writeback(const WritebackArgs &, int, hipStream_t) { return hi
 hipError_t launch_copy(void *, const void *, int64_t, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_norm(const NormArgs &, double *, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_clip(const double *, int32_t, float, float *, double *, hipStream_t) { return hipErrorNoDevice; }
-hipError_t launch_gather(const GatherArgs &, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_gather(const GatherArgs &, int, hipStream_t) { return hipErrorNoDevice; }
 }
 
 int main() {

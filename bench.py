@@ -371,6 +371,12 @@ def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> d
         "elements": E, "kernel_avg_us": t_pre * 1e6, "achieved_gbps": E * 28 / t_pre / 1e9,
         "frac": E * 28 / t_pre / 1e9 / PEAK_HBM_GBPS, "elements_per_s": E / t_pre}
     log(f"pre-reduced step (n_grads = 1): {t_pre * 1e6:.1f} us, {E * 28 / t_pre / 1e9:.0f} GB/s algorithmic")
+    # the write-back alone (bf16(master) into the owned elements): 4 + 2
+    # bytes per owned element
+    t_wb = timed(lambda: zdo.writeback_params(plan, st[0], par, coords, stream=stream))
+    out["writeback_params"] = {"bytes_per_element": 6, "elements": E, "kernel_avg_us": t_wb * 1e6,
+                               "achieved_gbps": E * 6 / t_wb / 1e9, "frac": E * 6 / t_wb / 1e9 / PEAK_HBM_GBPS}
+    log(f"writeback_params: {t_wb * 1e6:.1f} us, {E * 6 / t_wb / 1e9:.0f} GB/s algorithmic")
     out["clipped_step"] = {
         "path": "grad_norm_sq (writes the reduced gradient) + clip_coefficient + sharded_adam_step_clipped "
                 "(n_grads = 1)",

@@ -12,7 +12,7 @@
 namespace zdo {
 hipError_t launch_reduce(const ReduceArgs &, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_step(const StepArgs &, int, hipStream_t) { return hipErrorNoDevice; }
-hipError_t launch_writeback(const WritebackArgs &, int, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_writeback(const WritebackArgs &, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_copy(void *, const void *, int64_t, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_norm(const NormArgs &, double *, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_clip(const double *, int32_t, float, float *, double *, hipStream_t) { return hipErrorNoDevice; }

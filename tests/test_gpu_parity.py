@@ -436,10 +436,11 @@ def test_workload_every_rank_full_compare(gpu, name):
 
 def test_state_beyond_the_infinity_cache(gpu):
     """A shard whose fp32 state (12 bytes per slot) exceeds 256 MiB, the
-    Infinity Cache, takes the step's non-temporal state accesses: GPT-2
-    small's parameters plus three ragged ones at D = 4 (L about 31 M slots,
-    373 MB of state), rank 1 in WORLD and rank 3 in LOCAL coordinates, every
-    element compared, main grad included."""
+    Infinity Cache, takes the step's and the write-back's non-temporal state
+    accesses: GPT-2 small's parameters plus three ragged ones at D = 4 (L
+    about 31 M slots, 373 MB of state), rank 1 in WORLD and rank 3 in LOCAL
+    coordinates, every element compared, main grad included; then
+    writeback_params of the updated master equals the step's parameters."""
     sizes = W.gpt2_small_params() + [4093, 1, 77777]
     bucket, D = 40_000_000, 4
     lay = OL.build_layout(sizes, bucket, D)
@@ -453,8 +454,15 @@ def test_state_beyond_the_infinity_cache(gpu):
         state = [W.f32_host(W.normal_f32(Ln, 0.02, W.seed(2, 5, "master", r), DEV)),
                  W.f32_host(W.normal_f32(Ln, 1e-3, W.seed(2, 5, "m", r), DEV)),
                  W.f32_host(W.square_normal_f32(Ln, 1e-3, W.seed(2, 5, "v", r), DEV))]
-        run_rank_step(gpu, sizes, bucket, D, r, reps_h, state, 1.0 / D, hp, 3, c, c,
-                      reps_d=reps_d if c == gpu.WORLD else None)
+        new_state, par_h = run_rank_step(gpu, sizes, bucket, D, r, reps_h, state, 1.0 / D, hp, 3, c, c,
+                                         reps_d=reps_d if c == gpu.WORLD else None)
+        # writeback_params of the updated master (non-temporal loads here)
+        # gives the step's parameter bytes, sentinels elsewhere included
+        plan = gpu.build_range_map(sizes, bucket, D, r)
+        par2 = torch.full((par_h.size,), SENTINEL, dtype=torch.int16, device=DEV)
+        gpu.writeback_params(plan, to_dev(new_state[0]), par2, c)
+        assert_bf16(host_u16(par2), par_h, f"writeback_params r={r}")
+        del par2
         free()
     del reps_d
     free()

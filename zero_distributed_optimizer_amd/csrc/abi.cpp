@@ -535,7 +535,8 @@ int writeback_params(const zdo_plan *plan, const float *master, uint16_t *param_
     a.param_local = param_coords == ZDO_LOCAL;
     a.master = master;
     a.param = param_out;
-    return launch_result(launch_writeback(a, plan->lds_per_cu, static_cast<hipStream_t>(stream)), fn);
+    a.state_numel = plan->shard_numel;
+    return launch_result(launch_writeback(a, static_cast<hipStream_t>(stream)), fn);
 }
 
 int all_gather_params(const zdo_plan *plan, const uint16_t *const *params, int32_t n_params, uint16_t *out,

@@ -83,13 +83,14 @@ struct WritebackArgs {
     int32_t param_local;
     const float *master;
     uint16_t *param;
+    int64_t state_numel;  // L: the master array's length (selects its cache policy)
 };
 
 // lds_per_cu: LDS bytes per compute unit of the launch device (0 if unknown),
 // used to cap how many workgroups share a compute unit.
 hipError_t launch_reduce(const ReduceArgs &a, int lds_per_cu, hipStream_t stream);
 hipError_t launch_step(const StepArgs &a, int lds_per_cu, hipStream_t stream);
-hipError_t launch_writeback(const WritebackArgs &a, int lds_per_cu, hipStream_t stream);
+hipError_t launch_writeback(const WritebackArgs &a, hipStream_t stream);
 hipError_t launch_copy(void *dst, const void *src, int64_t n16, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs &a, int lds_per_cu, hipStream_t stream);
 // Squared norm: per-tile partials into a.partial, then their fixed-order sum

@@ -612,6 +612,9 @@ __global__ __launch_bounds__(64) void clip_kernel(const double *parts, int32_t n
     *coeff = float(q < 1.0 ? q : 1.0);
 }
 
+// kNT: master is loaded non-temporally (the state does not fit the
+// Infinity Cache), as in the step.
+template <bool kNT>
 __global__ __launch_bounds__(kBlock) void writeback_kernel(WritebackArgs a) {
     for (int64_t tile = a.walk.tile_begin + blockIdx.x; tile < a.walk.tile_begin + a.walk.ntiles;
          tile += gridDim.x) {
@@ -620,7 +623,7 @@ __global__ __launch_bounds__(kBlock) void writeback_kernel(WritebackArgs a) {
             continue;
         const int64_t pi = a.param_local ? c.k0 : c.w0;
         if (c.lo == 0 && c.hi == kChunk) {
-            const f32x4 x0 = ldf4(a.master + c.k0), x1 = ldf4(a.master + c.k0 + 4);
+            const f32x4 x0 = ld_state<kNT>(a.master + c.k0), x1 = ld_state<kNT>(a.master + c.k0 + 4);
             u32x4 o = {to_bf16x2(x0[0], x0[1]), to_bf16x2(x0[2], x0[3]), to_bf16x2(x1[0], x1[1]),
                        to_bf16x2(x1[2], x1[3])};
             st16_out(a.param + pi, o);
@@ -805,11 +808,20 @@ hipError_t launch_step(const StepArgs &a, int lds_per_cu, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_writeback(const WritebackArgs &a, int lds_per_cu, hipStream_t stream) {
+hipError_t launch_writeback(const WritebackArgs &a, hipStream_t stream) {
     if (a.walk.ntiles <= 0)
         return hipSuccess;
-    hipLaunchKernelGGL(writeback_kernel, dim3(grid_for(a.walk.ntiles)), dim3(kBlock),
-                       lds_reserve(lds_per_cu, a.walk.ntiles), stream, a);
+    // A tile moves 3 KiB: no occupancy cap, so that enough bytes are in
+    // flight (Llama-3-8B shape, non-temporal master: 1150 us at 16 waves
+    // per compute unit, 966 at 24, 964-967 uncapped; GPT-2 shape, plain
+    // loads: 17.2 us at 16, 15.5 uncapped). The master array goes
+    // non-temporal on the step's rule (Llama-3-8B uncapped: 1004-1007 us
+    // with plain loads; GPT-2: 16.2 us with non-temporal ones).
+    const dim3 grid(grid_for(a.walk.ntiles)), block(kBlock);
+    if (a.state_numel * int64_t(3 * sizeof(float)) > ZDO_STATE_CACHE_BYTES)
+        hipLaunchKernelGGL(writeback_kernel<true>, grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL(writeback_kernel<false>, grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

@@ -18,8 +18,9 @@
 //
 // HBM serves this mix of many read streams and some write streams best when
 // few requestors share it: one-wave workgroups, a number per compute unit
-// capped by the launch's length (see lds_reserve), non-temporal loads of
-// what is read once.
+// capped by the kernel and the launch's length (see lds_reserve; kernels
+// that move only a few KiB per tile take more waves or none), non-temporal
+// loads of what is read once.
 //
 // Arithmetic is fixed (contraction off, IEEE division and square root,
 // fp32 subnormals kept) so that results match a sequential CPU evaluation bit

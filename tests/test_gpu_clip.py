@@ -237,3 +237,44 @@ def test_found_inf_skips_every_rank(gpu):
     norm, c = _end_to_end(gpu, w, reps_d, reps_h, 1.0)
     assert not np.isfinite(norm) and np.isnan(c)
     free()
+
+
+def test_clipped_step_state_beyond_the_infinity_cache(gpu):
+    """The clipped step on a shard whose fp32 state exceeds 256 MiB (the
+    non-temporal state path): GPT-2 small's parameters plus three ragged ones
+    at D = 4, rank 2 (about 31 M slots), coefficient 0.3721 against the
+    oracle element by element; a NaN coefficient changes nothing."""
+    sizes = W.gpt2_small_params() + [4093, 1, 77777]
+    bucket, D, r = 40_000_000, 4, 2
+    lay = OL.build_layout(sizes, bucket, D)
+    N = lay.buffer_numel
+    reps_d = [W.normal_bf16(N, 1e-3, W.seed(2, 6, "grad", j), DEV).view(torch.int16) for j in range(D)]
+    reps_h = [host_u16(x) for x in reps_d]
+    hp = W.get("gpt2_small").hp
+    plan = gpu.build_range_map(sizes, bucket, D, r)
+    Ln = plan.shard_numel
+    assert 12 * Ln > 256 << 20
+    st0 = [W.normal_f32(Ln, 0.02, W.seed(2, 6, "master"), DEV), W.normal_f32(Ln, 1e-3, W.seed(2, 6, "m"), DEV),
+           W.square_normal_f32(Ln, 1e-3, W.seed(2, 6, "v"), DEV)]
+    st0_h = [host_f32(x) for x in st0]
+    c = float(np.float32(0.3721))
+    st = [x.clone() for x in st0]
+    par = torch.full((N,), SENTINEL, dtype=torch.int16, device=DEV)
+    gpu.sharded_adam_step_clipped(plan, reps_d, gpu.WORLD, 1.0 / D, *st, par, gpu.WORLD,
+                                  grad_coeff=torch.tensor([c], dtype=torch.float32, device=DEV), **hp_kwargs(hp, 2))
+    want = [x.copy() for x in st0_h]
+    want_par = np.full(N, SENTINEL, np.uint16)
+    OS.rank_step(lay, r, reps_h, OS.WORLD, 1.0 / D, *want, ON.hp_array(hp, 2), want_par, OS.WORLD, grad_coeff=c)
+    for got, w, nm in zip(st, want, ("master", "exp_avg", "exp_avg_sq")):
+        assert_f32(host_f32(got), w, f"c={c} {nm}")
+    assert_bf16(host_u16(par), want_par, f"c={c} params")
+    st = [x.clone() for x in st0]
+    par = torch.full((N,), SENTINEL, dtype=torch.int16, device=DEV)
+    gpu.sharded_adam_step_clipped(plan, reps_d, gpu.WORLD, 1.0 / D, *st, par, gpu.WORLD,
+                                  grad_coeff=torch.tensor([float("nan")], dtype=torch.float32, device=DEV),
+                                  **hp_kwargs(hp, 2))
+    for a, b in zip(st, st0):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert bool((par == SENTINEL).all())
+    del reps_d, st, st0, par
+    free()

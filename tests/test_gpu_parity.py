@@ -513,12 +513,13 @@ def _sample_slots(plan, rng, n):
     return np.unique(np.concatenate([slots] + edges))
 
 
-@pytest.mark.parametrize("name,coords", [("llama3_8b", "world"), ("llama3_70b", "local")])
+@pytest.mark.parametrize("name,coords", [("llama3_8b", "world"), ("llama3_8b", "local"), ("llama3_70b", "local")])
 def test_llama_shard_sampled(gpu, name, coords):
     """Llama-3-8B (D = 8) and Llama-3-70B (D = 32) shapes, one rank, the
-    full-size launch. 8B: D whole replica buffers and a whole parameter buffer
-    of N = 8.03e9 elements (WORLD coordinates, offsets beyond 2^32); 70B: the
-    rank's D replica slices and parameter slice (LOCAL). Compared with the
+    full-size launch. 8B in WORLD coordinates: D whole replica buffers and a
+    whole parameter buffer of N = 8.03e9 elements (offsets beyond 2^32); 8B
+    and 70B in LOCAL coordinates, as bench.py times them: the rank's D
+    replica slices and parameter slice. Compared with the
     oracle on 2^20 sampled owned slots plus every piece's first and last 16
     elements; every owned parameter slot written, no other one."""
     w = W.get(name)

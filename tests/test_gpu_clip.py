@@ -240,12 +240,13 @@ def test_found_inf_skips_every_rank(gpu):
 
 
 def test_clipped_step_state_beyond_the_infinity_cache(gpu):
-    """The clipped step on a shard whose fp32 state exceeds 256 MiB (the
-    non-temporal state path): GPT-2 small's parameters plus three ragged ones
-    at D = 4, rank 2 (about 31 M slots), coefficient 0.3721 against the
-    oracle element by element; a NaN coefficient changes nothing."""
-    sizes = W.gpt2_small_params() + [4093, 1, 77777]
-    bucket, D, r = 40_000_000, 4, 2
+    """The clipped step on a shard whose fp32 state exceeds 1 GiB (the
+    non-temporal state path): GPT-2 small's parameters twice over plus three
+    ragged ones at D = 2, rank 1 (about 124 M slots), coefficient 0.3721
+    against the oracle element by element; a NaN coefficient changes
+    nothing."""
+    sizes = W.gpt2_small_params() * 2 + [4093, 1, 77777]
+    bucket, D, r = 40_000_000, 2, 1
     lay = OL.build_layout(sizes, bucket, D)
     N = lay.buffer_numel
     reps_d = [W.normal_bf16(N, 1e-3, W.seed(2, 6, "grad", j), DEV).view(torch.int16) for j in range(D)]
@@ -253,7 +254,7 @@ def test_clipped_step_state_beyond_the_infinity_cache(gpu):
     hp = W.get("gpt2_small").hp
     plan = gpu.build_range_map(sizes, bucket, D, r)
     Ln = plan.shard_numel
-    assert 12 * Ln > 256 << 20
+    assert 12 * Ln > 1 << 30
     st0 = [W.normal_f32(Ln, 0.02, W.seed(2, 6, "master"), DEV), W.normal_f32(Ln, 1e-3, W.seed(2, 6, "m"), DEV),
            W.square_normal_f32(Ln, 1e-3, W.seed(2, 6, "v"), DEV)]
     st0_h = [host_f32(x) for x in st0]

@@ -435,22 +435,23 @@ def test_workload_every_rank_full_compare(gpu, name):
 
 
 def test_state_beyond_the_infinity_cache(gpu):
-    """A shard whose fp32 state (12 bytes per slot) exceeds 256 MiB, the
-    Infinity Cache, takes the step's and the write-back's non-temporal state
-    accesses: GPT-2 small's parameters plus three ragged ones at D = 4 (L
-    about 31 M slots, 373 MB of state), rank 1 in WORLD and rank 3 in LOCAL
-    coordinates, every element compared, main grad included; then
-    writeback_params of the updated master equals the step's parameters."""
-    sizes = W.gpt2_small_params() + [4093, 1, 77777]
-    bucket, D = 40_000_000, 4
+    """A shard whose fp32 state (12 bytes per slot) exceeds 1 GiB, well
+    beyond the 256 MB Infinity Cache, takes the step's and the write-back's
+    non-temporal state accesses: GPT-2 small's parameters twice over plus
+    three ragged ones at D = 2 (L about 124 M slots, 1.49 GB of state), rank
+    1 in WORLD and rank 0 in LOCAL coordinates, every element compared, main
+    grad included; then writeback_params of the updated master equals the
+    step's parameters."""
+    sizes = W.gpt2_small_params() * 2 + [4093, 1, 77777]
+    bucket, D = 40_000_000, 2
     lay = OL.build_layout(sizes, bucket, D)
     N = lay.buffer_numel
     reps_d = [W.normal_bf16(N, 1e-3, W.seed(2, 5, "grad", j), DEV).view(torch.int16) for j in range(D)]
     reps_h = [host_u16(x) for x in reps_d]
     hp = W.get("gpt2_small").hp
-    for r, c in ((1, gpu.WORLD), (3, gpu.LOCAL)):
+    for r, c in ((1, gpu.WORLD), (0, gpu.LOCAL)):
         Ln = OL.shard_numel(lay, r)
-        assert 12 * Ln > 256 << 20
+        assert 12 * Ln > 1 << 30
         state = [W.f32_host(W.normal_f32(Ln, 0.02, W.seed(2, 5, "master", r), DEV)),
                  W.f32_host(W.normal_f32(Ln, 1e-3, W.seed(2, 5, "m", r), DEV)),
                  W.f32_host(W.square_normal_f32(Ln, 1e-3, W.seed(2, 5, "v", r), DEV))]

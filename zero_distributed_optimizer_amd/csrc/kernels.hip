@@ -60,13 +60,13 @@ __device__ __forceinline__ uint32_t to_bf16x2(float a, float b) {
 // reduced gradient, main grad) are non-temporal stores too (Llama-3-8B-shaped
 // step: 6.83 ms in every run against 6.83-7.48 ms with plain stores;
 // Llama-3-70B-shaped reduce-scatter 7% faster). The fp32 state is read and
-// then rewritten. When it fits the 256 MB Infinity Cache, plain loads and
-// stores let the next step find it there (GPT-2-shaped step, 187 MB of
+// then rewritten. While it is at most a few times the 256 MB Infinity
+// Cache, plain loads and stores serve it best (GPT-2-shaped step, 187 MB of
 // state, back to back: 97.5 us against 109.8 us with non-temporal state
-// accesses). When it does not, the step loads and stores it non-temporally
-// as well (Llama-3-8B-shaped step: 6.92-6.98 -> 6.75-6.77 ms); non-temporal
-// stores after plain loads of the same lines are far slower than either
-// (3.4-3.6 TB/s).
+// accesses). Beyond 1 GiB (see launch_step) the step loads and stores it
+// non-temporally as well (Llama-3-8B-shaped step: 6.92-6.98 -> 6.75-6.77
+// ms); non-temporal stores after plain loads of the same lines are far
+// slower than either (3.4-3.6 TB/s).
 __device__ __forceinline__ u32x4 ld_rep(const uint16_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
@@ -475,8 +475,8 @@ __device__ __forceinline__ void step_slots(const StepArgs &a, const Quad &q, boo
 // kInst: a.rep holds a.ninst instances of D (or, for D = 0, a.dinst)
 // contributions each; otherwise a.nrep contributions of one instance.
 //
-// kNT: the fp32 state is loaded and stored non-temporally (it does not fit
-// the Infinity Cache; see the memory helpers above).
+// kNT: the fp32 state is loaded and stored non-temporally (it exceeds
+// 1 GiB; see launch_step).
 //
 // The occupancy bounds tell the compiler how many waves can share a SIMD,
 // which the launches cap anyway (lds_reserve): with at most 4 (3 for 32
@@ -613,8 +613,8 @@ __global__ __launch_bounds__(64) void clip_kernel(const double *parts, int32_t n
     *coeff = float(q < 1.0 ? q : 1.0);
 }
 
-// kNT: master is loaded non-temporally (the state does not fit the
-// Infinity Cache), as in the step.
+// kNT: master is loaded non-temporally (the state exceeds 1 GiB), as in
+// the step.
 template <bool kNT>
 __global__ __launch_bounds__(kBlock) void writeback_kernel(WritebackArgs a) {
     for (int64_t tile = a.walk.tile_begin + blockIdx.x; tile < a.walk.tile_begin + a.walk.ntiles;
@@ -763,10 +763,17 @@ hipError_t launch_reduce(const ReduceArgs &a, int lds_per_cu, hipStream_t stream
     return hipGetLastError();
 }
 
-// The fp32 state goes non-temporal when it cannot stay in the Infinity
-// Cache between steps.
+// The fp32 state goes non-temporal above 1 GiB (12 bytes per shard slot).
+// Measured on one box, plain -> non-temporal state, step time with cold
+// caches (back to back in brackets): 187 MB 102 -> 112 us (97 -> 109),
+// 299 MB 148 -> 159 us (150 -> 155), 498 MB 209 -> 218 us (235 -> 216),
+// 747 MB 296 -> 308 us (323 -> 307), 1.49 GB 582 -> 562 us (603 -> 565),
+// 3.0 GB 4.09 -> 3.99 ms, 6.0 GB 4.91 -> 4.73 ms, 12 GB 6.96 -> 6.76 ms.
+// Between steps of a training run the caches are cold, and there
+// non-temporal accesses pay off once the state is well beyond the 256 MB
+// Infinity Cache.
 #ifndef ZDO_STATE_CACHE_BYTES
-#define ZDO_STATE_CACHE_BYTES (int64_t(256) << 20)
+#define ZDO_STATE_CACHE_BYTES (int64_t(1) << 30)
 #endif
 
 template <bool kNT>

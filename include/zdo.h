@@ -25,9 +25,16 @@
  *     scalars: naturally aligned), and point to memory of the device the
  *     plan was built on. Host arrays (the replica pointer list, param_numel,
  *     hp) are read during the call only.
- *   - `stream` is a hipStream_t (NULL = the default stream). Calls that take
- *     one only enqueue work on it and return; they never allocate device
- *     memory and never synchronise the host.
+ *   - `stream` is a hipStream_t passed as void * (NULL = the default
+ *     stream), so that this header needs no HIP header; a hipStream_t
+ *     converts to it implicitly. Calls that take one only enqueue work on it
+ *     and return; they never allocate device memory and never synchronise
+ *     the host.
+ *   - A launch captured into a HIP graph replays with the arguments of its
+ *     capture. For the Adam calls these include the bias corrections of
+ *     hp->step, formed on the host at the call: a captured step is valid
+ *     for that one t, and a graph that replays several steps needs one
+ *     capture per t.
  *   - Coordinates of a buffer: ZDO_WORLD indexes the whole padded buffer
  *     [0, N); ZDO_LOCAL indexes the rank's shard [0, L).
  *   - The contributions a call sums (n_replicas / n_grads, 1..ZDO_MAX_REPLICAS,
@@ -145,6 +152,15 @@ int32_t zdo_plan_rank(const zdo_plan *plan);
 /* Two-call queries: with out == NULL (or cap too small) only *n is set. */
 int zdo_plan_buckets(const zdo_plan *plan, zdo_bucket *out, int32_t cap, int32_t *n);
 int zdo_plan_pieces(const zdo_plan *plan, zdo_piece *out, int64_t cap, int64_t *n);
+
+/* The same five plan calls under the short names of the range-map interface
+ * (page 1, §4.1: the map builders and their Range tables). Each is the
+ * zdo_-prefixed call above, with the same arguments, results and errors. */
+int plan_buckets(const zdo_plan *plan, zdo_bucket *out, int32_t cap, int32_t *n);
+int plan_pieces(const zdo_plan *plan, zdo_piece *out, int64_t cap, int64_t *n);
+int64_t plan_buffer_numel(const zdo_plan *plan);
+int64_t plan_shard_numel(const zdo_plan *plan);
+void plan_destroy(zdo_plan *plan);
 
 /* ---- device work ---------------------------------------------------------- */
 

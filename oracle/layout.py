@@ -27,9 +27,10 @@ Readings where the page leaves a step open (each also listed in the design doc):
   * A bucket's padding sits at its tail, up to the next multiple of D.
   * The rank's fp32 shard (master, m, v) concatenates the per-bucket local
     views in bucket order, each placed at the first slot >= the previous
-    end whose index is congruent to the range's world start modulo 8; so
-    every shard index is congruent to its world index modulo 8. The gap
-    slots (< 8 per bucket) and the padding slots are never read or written.
+    end whose index is congruent to the range's world start modulo 64
+    (SHARD_PHASE); so every shard index is congruent to its world index
+    modulo 64. The gap slots (< 64 per bucket) and the padding slots are
+    never read or written.
 """
 
 from __future__ import annotations

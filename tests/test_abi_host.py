@@ -27,7 +27,7 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     L = Z.require_library()
     names = header_functions()
-    assert len(names) == 23, names
+    assert len(names) == 28, names
     assert sorted(Z.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -35,6 +35,35 @@ def test_library_exports_every_declared_symbol():
     for n in ("build_range_map", "reduce_scatter_local", "force_all_reduce", "sharded_adam_step",
               "writeback_params"):
         assert callable(getattr(Z, n))
+
+
+def test_short_plan_names_equal_the_prefixed_ones():
+    """plan_buckets, plan_pieces, plan_buffer_numel, plan_shard_numel and
+    plan_destroy answer exactly as their zdo_plan_ twins (host-only plan)."""
+    L = Z.require_library()
+    w = W.get("frag")
+    sizes = np.ascontiguousarray(np.asarray(w.param_numel[:3000], dtype=np.int64))
+    h = ctypes.c_void_p()
+    rc = L.build_range_map(sizes.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), int(sizes.size),
+                           400_000, 16, 5, ctypes.byref(h))
+    assert rc == 0
+    try:
+        assert L.plan_buffer_numel(h) == L.zdo_plan_buffer_numel(h) > 0
+        assert L.plan_shard_numel(h) == L.zdo_plan_shard_numel(h) > 0
+        for short, long_, dt, ct in ((L.plan_buckets, L.zdo_plan_buckets, Z.BUCKET_DTYPE, ctypes.c_int32),
+                                     (L.plan_pieces, L.zdo_plan_pieces, Z.PIECE_DTYPE, ctypes.c_int64)):
+            n1, n2 = ct(), ct()
+            assert short(h, None, 0, ctypes.byref(n1)) == 0 == long_(h, None, 0, ctypes.byref(n2))
+            assert n1.value == n2.value > 0
+            a, b = np.zeros(n1.value, dt), np.zeros(n2.value, dt)
+            assert short(h, a.ctypes.data, n1.value, ctypes.byref(n1)) == 0
+            assert long_(h, b.ctypes.data, n2.value, ctypes.byref(n2)) == 0
+            assert a.tobytes() == b.tobytes()
+        assert L.plan_buckets(None, None, 0, ctypes.byref(ctypes.c_int32())) == Z.EINVAL
+        assert L.plan_buffer_numel(None) == -1 and L.plan_shard_numel(None) == -1
+    finally:
+        L.plan_destroy(h)
+    L.plan_destroy(None)
 
 
 def test_struct_layouts():

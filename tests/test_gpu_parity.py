@@ -500,84 +500,6 @@ def test_buffers_object_equals_tensor_lists(gpu):
     free()
 
 
-def _sample_slots(plan, rng, n):
-    """Owned LOCAL slots: random ones plus the first and last 16 of every piece."""
-    pcs = plan.pieces()
-    starts = pcs["shard_offset"].astype(np.int64)
-    lens = (pcs["gbuf_world"][:, 1] - pcs["gbuf_world"][:, 0]).astype(np.int64)
-    cum = np.concatenate([[0], np.cumsum(lens)])
-    pick = rng.integers(0, cum[-1], size=n)
-    pi = np.searchsorted(cum, pick, side="right") - 1
-    slots = starts[pi] + (pick - cum[pi])
-    edges = [np.arange(s, s + min(16, l)) for s, l in zip(starts, lens)] + \
-            [np.arange(s + max(0, l - 16), s + l) for s, l in zip(starts, lens)]
-    return np.unique(np.concatenate([slots] + edges))
-
-
-@pytest.mark.parametrize("name,coords", [("llama3_8b", "world"), ("llama3_8b", "local"), ("llama3_70b", "local")])
-def test_llama_shard_sampled(gpu, name, coords):
-    """Llama-3-8B (D = 8) and Llama-3-70B (D = 32) shapes, one rank, the
-    full-size launch. 8B in WORLD coordinates: D whole replica buffers and a
-    whole parameter buffer of N = 8.03e9 elements (offsets beyond 2^32); 8B
-    and 70B in LOCAL coordinates, as bench.py times them: the rank's D
-    replica slices and parameter slice. Compared with the
-    oracle on 2^20 sampled owned slots plus every piece's first and last 16
-    elements; every owned parameter slot written, no other one."""
-    w = W.get(name)
-    r = w.verify_ranks[0]
-    plan = gpu.build_range_map(w.param_numel, w.bucket_numel, w.dp_size, r)
-    Ln, N = plan.shard_numel, plan.buffer_numel
-    world = coords == "world"
-    C = gpu.WORLD if world else gpu.LOCAL
-    n_rep = N if world else Ln
-    stride = local_stride(n_rep)
-    pcs = plan.pieces()
-    reps = []
-    if world:
-        bufs = torch.empty(w.dp_size * stride, dtype=torch.bfloat16, device=DEV)
-        tmp = torch.empty(Ln, dtype=torch.bfloat16, device=DEV)
-        for j in range(w.dp_size):
-            W.normal_bf16(Ln, w.grad_sigma, W.seed(w.cfg, 0, "grad", j), out=tmp)
-            dst = bufs[j * stride: j * stride + N]
-            for p in pcs:
-                ws, we = int(p["gbuf_world"][0]), int(p["gbuf_world"][1])
-                k0 = int(p["shard_offset"])
-                dst[ws:we].copy_(tmp[k0:k0 + we - ws])
-            reps.append(dst.view(torch.int16))
-        del tmp
-    else:
-        bufs = torch.empty(w.dp_size * stride, dtype=torch.bfloat16, device=DEV)
-        for j in range(w.dp_size):
-            s = bufs[j * stride: j * stride + Ln]
-            W.normal_bf16(Ln, w.grad_sigma, W.seed(w.cfg, 0, "grad", j), out=s)
-            reps.append(s.view(torch.int16))
-    st = _gen_state(w, Ln)
-    par = torch.full((n_rep,), SENTINEL, dtype=torch.int16, device=DEV)
-    rng = np.random.default_rng(w.cfg)
-    ks = _sample_slots(plan, rng, 1 << 20)
-    # WORLD index of every sampled shard slot, through the range map
-    starts = pcs["shard_offset"].astype(np.int64)
-    order = np.argsort(starts)
-    pi = order[np.searchsorted(starts[order], ks, side="right") - 1]
-    ws = pcs["gbuf_world"][pi, 0].astype(np.int64) + (ks - starts[pi])
-    k = torch.from_numpy(ks).to(DEV)
-    gidx = torch.from_numpy(ws if world else ks).to(DEV)
-    before = [host_f32(x[k]) for x in st]
-    grads = [host_u16(x[gidx]) for x in reps]
-    gpu.sharded_adam_step(plan, reps, C, w.scale, *st, par, C, **hp_kwargs(w.hp, 1))
-    torch.cuda.synchronize()
-    want_par = np.zeros(k.numel(), np.uint16)
-    ON.step(grads, w.scale, *before, ON.hp_array(w.hp, 1), want_par)
-    for got, want, nm in zip(st, before, ("master", "exp_avg", "exp_avg_sq")):
-        assert_f32(host_f32(got[k]), want, f"{name} {nm}")
-    assert_bf16(host_u16(par[gidx]), want_par, f"{name} params")
-    # the sentinel is a NaN pattern, which no updated parameter is: it must
-    # survive exactly on the slots the rank does not own
-    assert int((par == SENTINEL).sum()) == n_rep - plan.owned_numel
-    del bufs, reps, st, par
-    free()
-
-
 # ---- edge cases of size and arithmetic --------------------------------------------------------
 
 @pytest.mark.parametrize("D", [64, 48])

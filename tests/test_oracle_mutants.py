@@ -66,6 +66,8 @@ def _layout_pins():
         TS.test_writeback_touches_owned_range_only,
         lambda: TS.test_all_gather_closes_the_zero1_loop(0),
         lambda: TS.test_all_gather_closes_the_zero1_loop(1),
+        lambda: TS.test_rank_norm_sq_exact_and_summing_to_the_global_norm(0),
+        lambda: TS.test_rank_norm_sq_exact_and_summing_to_the_global_norm(1),
     ]
 
 
@@ -198,6 +200,14 @@ PY_MUTANTS = {
         ("            r = L.rank_range(b, layout.dp_size, j)\n            out[r.start:r.end]",
          "            r = L.rank_range(b, layout.dp_size, j)\n            r = L.Range(r.start, min(r.end, b.offset + b.numel))\n"
          "            out[r.start:r.end]")]),
+    "squared norm read at the bucket-local offset": ("step", [
+        ("        g0, g1 = _span(grad_coords, pc.gbuf_world, pc.shard_offset)\n        total",
+         "        g0, g1 = _span(grad_coords, pc.gbuf_world, pc.gbuf_local.start)\n        total")]),
+    "squared norm over the whole rank range, padding included": ("step", [
+        ("    for pc in L.rank_pieces(layout, rank):\n        g0, g1 = _span(grad_coords, pc.gbuf_world, pc.shard_offset)\n"
+         "        total",
+         "    for world, base in L.rank_ranges(layout, rank):\n        g0, g1 = _span(grad_coords, world, base)\n"
+         "        total")]),
     "reduce-scatter over the parameter pieces only": ("step", [
         ("    for b, (world, base) in enumerate(L.rank_ranges(layout, rank)):",
          "    for b, (world, base) in enumerate([(pc.gbuf_world, pc.shard_offset)\n"

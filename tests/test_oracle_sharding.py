@@ -2,9 +2,10 @@
 pages fix about sharding:
   * page "04 · 分布式优化器", §2/§3: each rank updates only its range and the
     ranks together cover the buffer, so the union of the D rank steps must
-    equal the unsharded step, bit for bit (the "simulate the shards on the
-    CPU in sequence and compare with the dense result" pattern of the page
-    "Megatron-LM 与 ZeRO", section "最小语义 reference");
+    equal the unsharded step, bit for bit (the page "Megatron-LM 与 ZeRO",
+    section "最小语义 reference", checks sharding the same way: every shard
+    stepped on the CPU one after another, then compared with the dense
+    update);
   * §5: force_all_reduce yields the full reduced buffer, whose restriction
     to rank r's range is rank r's reduce-scatter;
   * §4.3: the write-back touches the owned range only.
@@ -354,3 +355,60 @@ def test_all_gather_closes_the_zero1_loop(seed):
     k = pr.randrange(D)
     S.all_gather(lay, bufs, bufs[k])
     assert np.array_equal(bufs[k], want)
+
+
+# ---- the rank's squared gradient norm (distributed-training notes, §8.3) -------------------------
+
+def _owner_scan(lay, D):
+    """For every element of the padded buffer: the rank that owns it and
+    whether a parameter sits there, found element by element from the
+    bucket table (page 1, §3: rank r holds the r-th of D equal ranges of a
+    padded bucket), without the range map."""
+    Nn = lay.buffer_numel
+    owner = np.full(Nn, -1, np.int64)
+    is_param = np.zeros(Nn, bool)
+    for b in lay.buckets:
+        S_b = b.padded_numel // D
+        for w in range(b.offset, b.offset + b.padded_numel):
+            owner[w] = (w - b.offset) // S_b
+            is_param[w] = w < b.offset + b.numel
+    return owner, is_param
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_rank_norm_sq_exact_and_summing_to_the_global_norm(seed):
+    """rank_norm_sq against an exact sum. Gradients are small integers (exact
+    in bf16) and the scale a power of two, so every reduced value and every
+    square is exact and the fp64 total is exact in any order. Padding holds
+    large non-zero values, so counting a padding element would change the
+    total. Checked in WORLD and LOCAL coordinates on multi-bucket padded
+    layouts, and the ranks' parts add up to the squared norm of the
+    all-reduced buffer over the parameter elements (padding excluded)."""
+    rng = np.random.default_rng(900 + seed)
+    D = int(rng.integers(2, 7))
+    sizes = [int(x) for x in rng.integers(1, 90, size=int(rng.integers(4, 12)))]
+    bucket = int(rng.integers(15, max(16, sum(sizes) // 3)))
+    lay = L.build_layout(sizes, bucket, D)
+    assert len(lay.buckets) > 1
+    assert any(b.padded_numel > b.numel for b in lay.buckets)
+    Nn = lay.buffer_numel
+    owner, is_param = _owner_scan(lay, D)
+    ints = [rng.integers(-8, 9, size=Nn) for _ in range(D)]
+    for g in ints:
+        g[~is_param] = 1000                 # padding: large, never counted
+    grads = [bf16(g.astype(np.float32)) for g in ints]
+    scale = 0.5
+    total_int = np.sum(ints, axis=0)        # exact integer sums
+    sq = (total_int.astype(np.float64) * scale) ** 2
+    global_sq = 0.0
+    for r in range(D):
+        want = float(np.sum(sq[(owner == r) & is_param]))
+        got_w = S.rank_norm_sq(lay, r, grads, S.WORLD, scale)
+        assert got_w == want, f"rank {r} WORLD: {got_w} != {want}"
+        loc = [S.local_slices(lay, r, g, fill=0x4000) for g in grads]   # 2.0 in the gap slots
+        got_l = S.rank_norm_sq(lay, r, loc, S.LOCAL, scale)
+        assert got_l == want, f"rank {r} LOCAL: {got_l} != {want}"
+        global_sq += got_w
+    red = N.widen(S.all_reduce(grads, scale)).astype(np.float64)
+    assert global_sq == float(np.sum(red[is_param] ** 2))
+    assert global_sq == float(np.sum(sq[is_param]))

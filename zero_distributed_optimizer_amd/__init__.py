@@ -68,7 +68,8 @@ EXPORTS = ("build_range_map", "zdo_plan_destroy", "zdo_plan_buffer_numel", "zdo_
            "zdo_plan_pieces", "reduce_scatter_local", "force_all_reduce", "sharded_adam_step",
            "writeback_params", "reduce_scatter_local_buckets", "sharded_adam_step_buckets",
            "zdo_plan_norm_workspace_bytes", "grad_norm_sq", "clip_coefficient", "sharded_adam_step_clipped",
-           "sharded_adam_step_instances", "all_gather_params", "zdo_device_copy", "zdo_last_error")
+           "sharded_adam_step_instances", "all_gather_params", "zdo_device_copy", "zdo_last_error",
+           "plan_buckets", "plan_pieces", "plan_buffer_numel", "plan_shard_numel", "plan_destroy")
 
 _lib = None
 
@@ -94,6 +95,13 @@ def require_library() -> ctypes.CDLL:
         getattr(L, f).restype = i32
     L.zdo_plan_buckets.argtypes = [vp, vp, i32, ctypes.POINTER(i32)]
     L.zdo_plan_pieces.argtypes = [vp, vp, i64, ctypes.POINTER(i64)]
+    L.plan_buckets.argtypes = [vp, vp, i32, ctypes.POINTER(i32)]
+    L.plan_pieces.argtypes = [vp, vp, i64, ctypes.POINTER(i64)]
+    for f in ("plan_buffer_numel", "plan_shard_numel"):
+        getattr(L, f).argtypes = [vp]
+        getattr(L, f).restype = i64
+    L.plan_destroy.argtypes = [vp]
+    L.plan_destroy.restype = None
     L.reduce_scatter_local.argtypes = [vp, vp, i32, i32, f32, vp, i32, vp]
     L.force_all_reduce.argtypes = [vp, vp, i32, f32, vp, vp]
     L.sharded_adam_step.argtypes = [vp, vp, i32, i32, f32, vp, vp, vp, vp, i32, ctypes.POINTER(Adam), vp, vp]
@@ -113,13 +121,35 @@ def require_library() -> ctypes.CDLL:
     L.zdo_device_copy.argtypes = [vp, vp, i64, vp]
     L.zdo_last_error.argtypes = []
     L.zdo_last_error.restype = ctypes.c_char_p
-    for f in ("build_range_map", "zdo_plan_buckets", "zdo_plan_pieces", "reduce_scatter_local",
+    for f in ("build_range_map", "zdo_plan_buckets", "zdo_plan_pieces", "plan_buckets", "plan_pieces",
+              "reduce_scatter_local",
               "force_all_reduce", "sharded_adam_step", "writeback_params", "grad_norm_sq", "clip_coefficient",
               "sharded_adam_step_clipped", "reduce_scatter_local_buckets", "sharded_adam_step_buckets",
               "sharded_adam_step_instances", "all_gather_params", "zdo_device_copy"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
+
+
+class use_library:
+    """Within the block, every call goes to the libzdo build at `path` (for
+    example one compiled with different launch caps); the previous library
+    is restored on exit. Plans made inside belong to that build and must be
+    destroyed inside the block."""
+
+    def __init__(self, path: str):
+        self.path = os.path.abspath(path)
+
+    def __enter__(self):
+        global _lib, LIB_PATH
+        self._saved = (_lib, LIB_PATH)
+        _lib, LIB_PATH = None, self.path
+        return require_library()
+
+    def __exit__(self, *exc):
+        global _lib, LIB_PATH
+        _lib, LIB_PATH = self._saved
+        return False
 
 
 def _check(rc: int) -> None:

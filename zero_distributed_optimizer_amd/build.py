@@ -18,6 +18,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libzdo.so")
+# A test build whose launches are capped at 64 workgroups, so that every
+# kernel walks its tiles through the grid-stride continuation (in the real
+# build only launches of more than 2^24 tiles do).
+GRID_LOOP_LIB = os.path.join(HERE, "libzdo_gridloop.so")
+GRID_LOOP_FLAGS = ["-DZDO_MAX_GRID=64"]
 SOURCES = ["plan.cpp", "abi.cpp", "kernels.hip"]
 HEADERS = ["zdo_internal.h", "kernels.h"]
 
@@ -55,5 +60,13 @@ def build(verbose: bool = False, extra: list[str] | None = None, out: str | None
     return out
 
 
+def build_all(verbose: bool = False) -> list[str]:
+    """The library and its grid-loop test build, compiled side by side."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(2) as ex:
+        jobs = [ex.submit(build, verbose), ex.submit(build, verbose, GRID_LOOP_FLAGS, GRID_LOOP_LIB)]
+        return [j.result() for j in jobs]
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build_all(verbose="-v" in sys.argv))

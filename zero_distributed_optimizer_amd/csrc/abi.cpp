@@ -219,6 +219,16 @@ int zdo_plan_pieces(const zdo_plan *p, zdo_piece *out, int64_t cap, int64_t *n) 
     return ZDO_OK;
 }
 
+int plan_buckets(const zdo_plan *p, zdo_bucket *out, int32_t cap, int32_t *n) {
+    return zdo_plan_buckets(p, out, cap, n);
+}
+int plan_pieces(const zdo_plan *p, zdo_piece *out, int64_t cap, int64_t *n) {
+    return zdo_plan_pieces(p, out, cap, n);
+}
+int64_t plan_buffer_numel(const zdo_plan *p) { return zdo_plan_buffer_numel(p); }
+int64_t plan_shard_numel(const zdo_plan *p) { return zdo_plan_shard_numel(p); }
+void plan_destroy(zdo_plan *p) { zdo_plan_destroy(p); }
+
 static int reduce_scatter_impl(const char *fn, const zdo_plan *plan, int32_t b0, int32_t b1,
                                const uint16_t *const *replicas, int32_t n_replicas, int32_t replica_coords,
                                float scale, uint16_t *out, int32_t out_coords, void *stream) {

@@ -685,8 +685,14 @@ __global__ __launch_bounds__(kBlock) void copy_kernel(u32x4 *dst, const u32x4 *s
 }
 
 // Enough blocks to cover every tile once, up to a cap that keeps the grid's
-// work-item count in range; larger launches loop over tiles.
-constexpr int64_t kMaxGrid = int64_t(1) << 24;
+// work-item count in range; larger launches loop over tiles (every kernel's
+// tile loop steps by gridDim.x). A build with a small cap makes every
+// launch take that loop.
+#ifndef ZDO_MAX_GRID
+#define ZDO_MAX_GRID (int64_t(1) << 24)
+#endif
+constexpr int64_t kMaxGrid = ZDO_MAX_GRID;
+static_assert(kMaxGrid >= 1 && kMaxGrid <= (int64_t(1) << 24), "grid cap out of range");
 
 unsigned grid_for(int64_t ntiles) {
     return unsigned(ntiles < kMaxGrid ? ntiles : kMaxGrid);

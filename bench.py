@@ -4,17 +4,30 @@
 A step is one sharded_adam_step call on the rank's shard: reduce the D
 replica contributions (scaled, fixed rank order), Adam on the fp32
 master/m/v shard, bf16 write-back into the owned range; one fused kernel.
-Default workload: GPT-2-small-shaped parameter list (124,439,808 elements,
-buckets of 40,000,000, D = 8), rank 1's shard (15,554,976 elements), 8 full
-bf16 replica buffers in HBM.
 
-Prints one JSON line: elements/s of the step (wall clock over the timed
-steps), the HBM roofline of the step kernel (algorithmic bytes (2D+26) per
-owned element over its average duration, from HIP events on the launch
-stream: one event pair around the timed steps, so that the average is the
-region over K), and the CPU oracle timed on a bounded sample beside it.
+Headline (default): the Llama-3-70B-shaped parameter list (723 tensors,
+70,553,706,496 elements, buckets of 200,000,000, D = 32), rank 1's shard of
+2,204,803,328 owned elements, its 32 bf16 contribution slices, fp32
+master/m/v and bf16 parameter slice resident in HBM (172 GB).
+
+Prints one JSON line:
+  * value: elements/s of the timed steps (wall clock), ms_per_step;
+  * roofline: the step kernel's algorithmic bytes, (2D + 26) per owned
+    element, over its average duration: one HIP event pair on the launch
+    stream around the K timed steps, divided by K; traffic: HBM bytes per
+    launch from the committed counter summary of the same kernel source;
+  * cold_cache: the step after 1 GiB of reads evicted the caches;
+  * variants: the library's other calls on the same shard;
+  * configs: every workload the step is measured on, rank by rank (Tiny
+    ranks 1..3, GPT-2 rank 1, Llama-3-8B rank 1, fragmentation ranks 0..15
+    and its force_all_reduce path). Where the fp32 state fits the 256 MB
+    Infinity Cache, back-to-back steps find part of it there; their HBM
+    figure is the cold-cache one, and the back-to-back one is labelled;
+  * cpu_baseline: the oracle on the host cores, streamed over the shard in
+    chunks of 2^26 slots (a bounded sample of them), and on one core.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--rank R]
+                    [--configs all|none] [--cpu-seconds S] [--no-cpu]
 """
 
 from __future__ import annotations
@@ -32,6 +45,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sharded Adam step: elements/s and HBM GB/s (% of peak) at 1 MI355X"
 PEAK_HBM_GBPS = 8000.0
+STATE_CACHE_BYTES = 1 << 30      # below this, a back-to-back step finds state in the Infinity Cache
+CPU_CHUNK = 1 << 26
 KERNEL_SOURCES = [os.path.join(ROOT, "zero_distributed_optimizer_amd", "csrc", f)
                   for f in ("kernels.hip", "kernels.h", "zdo_internal.h")]
 
@@ -64,15 +79,112 @@ def traffic_from_profiles(workload: str) -> float | None:
     return float(val.group(1))
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ---- inputs --------------------------------------------------------------------------------------
+
+class Shard:
+    """A rank's inputs resident in HBM: the D contributions (whole buffers
+    or shard slices, each on a 128-byte line), master/exp_avg/exp_avg_sq
+    and a parameter buffer."""
+
+    def __init__(self, zdo, torch, W, w, rank: int, dev, stagger: int = 0, reps=None):
+        self.w, self.rank = w, rank
+        self.plan = zdo.build_range_map(w.param_numel, w.bucket_numel, w.dp_size, rank)
+        p = self.plan
+        self.coords = zdo.WORLD if w.grad_mode == "world" else zdo.LOCAL
+        self.n_rep = p.buffer_numel if self.coords == zdo.WORLD else p.shard_numel
+        D, Ln = w.dp_size, p.shard_numel
+        if reps is None:
+            stride = (self.n_rep + 63) // 64 * 64
+            gap2 = stagger // 2
+            self.rep_buf = torch.empty(D * (stride + gap2), dtype=torch.bfloat16, device=dev)
+            reps = []
+            for j in range(D):
+                s = self.rep_buf[j * (stride + gap2): j * (stride + gap2) + self.n_rep]
+                W.normal_bf16(self.n_rep, w.grad_sigma, W.seed(w.cfg, 0, "grad", j), out=s,
+                              probe_fraction=w.probe_fraction, probe_seed=W.seed(w.cfg, 0, "probe", j))
+                reps.append(s.view(torch.int16))
+        self.reps = reps
+        sstride = (Ln + 31) // 32 * 32 + stagger // 4
+        self.state_buf = torch.empty(3 * sstride, dtype=torch.float32, device=dev)
+        self.state = [self.state_buf[i * sstride: i * sstride + Ln] for i in range(3)]
+        W.normal_f32(Ln, w.master_sigma, W.seed(w.cfg, 0, "master", rank), out=self.state[0])
+        W.normal_f32(Ln, w.m_sigma, W.seed(w.cfg, 0, "m", rank), out=self.state[1])
+        W.square_normal_f32(Ln, w.v_sigma, W.seed(w.cfg, 0, "v", rank), out=self.state[2])
+        self.params = torch.zeros(self.n_rep, dtype=torch.int16, device=dev)
+        self.t = 0
+        self.E = p.owned_numel
+        self.D = D
+        self.bytes_per_elem = 2 * D + 26
+        self.alg_bytes = self.E * self.bytes_per_elem
+        self.state_bytes = 12 * Ln
+
+    def step(self, zdo, stream) -> None:
+        self.t += 1
+        w = self.w
+        zdo.sharded_adam_step(self.plan, self.reps, self.coords, w.scale, *self.state, self.params, self.coords,
+                              step=self.t, stream=stream, **w.hp)
+
+
+def back_to_back(torch, fn, stream, n: int, warmup: int = 3) -> tuple:
+    """(seconds per call from one HIP event pair around n back-to-back calls
+    on the launch stream, seconds per call by wall clock)."""
+    for _ in range(warmup):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    a.record(stream)
+    for _ in range(n):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / 1e3 / n, (time.perf_counter() - w0) / n
+
+
+def cold(torch, np, fn, stream, flush_src, n: int) -> float:
+    """Seconds per call (mean over n) of calls each after 1 GiB of ordinary
+    (temporal) reads, which evict the 256 MB Infinity Cache and the L2s as a
+    training step's forward and backward passes would; the event pair
+    brackets the call only."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        flush_src.sum()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+
+
+def rate(alg_bytes: float, seconds: float) -> dict:
+    gbps = alg_bytes / seconds / 1e9
+    return {"us": seconds * 1e6, "gbps": gbps, "frac": gbps / PEAK_HBM_GBPS}
+
+
+# ---- main ------------------------------------------------------------------------------------
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="gpt2_small")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3_70b")
     ap.add_argument("--rank", type=int, default=None)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--configs", choices=("all", "none"), default="all",
+                    help="also time every other workload, rank by rank")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--stagger", type=int, default=0,
                     help="extra bytes (a multiple of 16) placed between consecutive input buffers")
     args = ap.parse_args()
@@ -80,6 +192,8 @@ def main() -> int:
         print(json.dumps({"error": "this build measures one GPU only: the D ranks' contributions are D "
                           "replica buffers in one GPU's HBM; run with --gpus 1"}), flush=True)
         return 2
+    if args.stagger % 16:
+        raise SystemExit("--stagger must be a multiple of 16")
 
     import numpy as np
     import torch
@@ -91,141 +205,81 @@ def main() -> int:
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
     w = W.get(args.workload)
     rank = w.time_ranks[0] if args.rank is None else args.rank
-    D = w.dp_size
-    plan = zdo.build_range_map(w.param_numel, w.bucket_numel, D, rank)
-    N, Ln, E = plan.buffer_numel, plan.shard_numel, plan.owned_numel
-    coords = zdo.WORLD if w.grad_mode == "world" else zdo.LOCAL
-    n_rep = N if coords == zdo.WORLD else Ln
-    stride = (n_rep + 63) // 64 * 64      # 128-byte-aligned replica buffers
-    log(f"workload {w.name}: N={N} D={D} rank={rank} E={E} L={Ln} grads={w.grad_mode}")
 
-    # inputs, resident in HBM before the timed region: the D replicas in one
-    # allocation, then the three state arrays in another, each buffer starting
-    # on a 128-byte line (plus `stagger` bytes further from the previous one)
-    if args.stagger % 16:
-        raise SystemExit("--stagger must be a multiple of 16")
     t0 = time.perf_counter()
-    gap2, gap4 = args.stagger // 2, args.stagger // 4
-    rep_buf = torch.empty(D * (stride + gap2), dtype=torch.bfloat16, device=dev)
-    reps = []
-    for j in range(D):
-        s = rep_buf[j * (stride + gap2): j * (stride + gap2) + n_rep]
-        W.normal_bf16(n_rep, w.grad_sigma, W.seed(w.cfg, 0, "grad", j), out=s,
-                      probe_fraction=w.probe_fraction, probe_seed=W.seed(w.cfg, 0, "probe", j))
-        reps.append(s.view(torch.int16))
-    sstride = (Ln + 31) // 32 * 32 + gap4
-    state_buf = torch.empty(3 * sstride, dtype=torch.float32, device=dev)
-    master, exp_avg, exp_avg_sq = (state_buf[i * sstride: i * sstride + Ln] for i in range(3))
-    W.normal_f32(Ln, w.master_sigma, W.seed(w.cfg, 0, "master"), out=master)
-    W.normal_f32(Ln, w.m_sigma, W.seed(w.cfg, 0, "m"), out=exp_avg)
-    W.square_normal_f32(Ln, w.v_sigma, W.seed(w.cfg, 0, "v"), out=exp_avg_sq)
-    params = torch.zeros(n_rep, dtype=torch.int16, device=dev)
+    sh = Shard(zdo, torch, W, w, rank, dev, args.stagger)
+    plan, E, D = sh.plan, sh.E, sh.D
     torch.cuda.synchronize(dev)
-    log(f"inputs generated in {time.perf_counter() - t0:.1f}s")
-
-    stream = torch.cuda.current_stream(dev)
-    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
-
-    def step(t: int) -> None:
-        zdo.sharded_adam_step(plan, reps, coords, w.scale, master, exp_avg, exp_avg_sq, params, coords,
-                              step=t, stream=stream, **hp)
-
-    t = 0
-    for _ in range(args.warmup):
-        t += 1
-        step(t)
-    torch.cuda.synchronize(dev)
+    log(f"workload {w.name}: N={plan.buffer_numel} D={D} rank={rank} E={E} L={plan.shard_numel} "
+        f"grads={w.grad_mode}; inputs generated in {time.perf_counter() - t0:.1f}s")
 
     # timed region: K back-to-back steps between one HIP event pair on the
-    # launch stream; the average launch duration is the region over K. An
-    # event pair around every launch would drain the queue before and after
-    # each step and slow the steps it measures (GPT-2 shape: 96.8 us per step
-    # back to back, 98.7-99.6 us per step between per-launch pairs)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize(dev)
-    w0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        t += 1
-        step(t)
-    ev1.record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - w0
-    ms_per_step = wall * 1e3 / args.steps
-    kern_avg_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
-    bytes_per_elem = 2 * D + 26
-    alg_bytes = E * bytes_per_elem
-    achieved = alg_bytes / kern_avg_s / 1e9
-    log(f"step: wall {ms_per_step * 1e3:.1f} us/step, kernel avg {kern_avg_s * 1e6:.1f} us, "
-        f"{achieved:.0f} GB/s algorithmic")
+    # launch stream (bracketed by synchronisations); the average launch
+    # duration is the region over K. An event pair around every launch would
+    # drain the queue before and after each step and slow the steps it
+    # measures.
+    for _ in range(args.warmup):
+        sh.step(zdo, stream)
+    kern_s, wall_s = back_to_back(torch, lambda: sh.step(zdo, stream), stream, args.steps, warmup=0)
+    ms_per_step = wall_s * 1e3
+    achieved = sh.alg_bytes / kern_s / 1e9
+    log(f"step: wall {wall_s * 1e6:.1f} us/step, kernel avg {kern_s * 1e6:.1f} us, {achieved:.0f} GB/s "
+        f"algorithmic ({achieved / PEAK_HBM_GBPS:.1%} of 8 TB/s)")
 
-    # after the timed region: single launches between their own event pairs,
-    # for the spread of one launch's duration
-    n_iso = min(args.steps, 50)
+    # single launches between their own event pairs: the spread of one launch
+    n_iso = min(args.steps, 20)
     iev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_iso)]
     for a, b in iev:
-        t += 1
         a.record(stream)
-        step(t)
+        sh.step(zdo, stream)
         b.record(stream)
     torch.cuda.synchronize(dev)
     iso_ms = [a.elapsed_time(b) for a, b in iev]
     isolated = {"steps": n_iso, "avg_us": float(np.mean(iso_ms)) * 1e3,
                 "p10_us": float(np.percentile(iso_ms, 10)) * 1e3, "p90_us": float(np.percentile(iso_ms, 90)) * 1e3,
                 "how": "each launch between its own event pair, after the timed region"}
-    log(f"single launches: avg {isolated['avg_us']:.1f} us (p10 {isolated['p10_us']:.1f}, "
-        f"p90 {isolated['p90_us']:.1f})")
 
     # plain-copy reference on the same stream (1 GiB read + 1 GiB write)
     nb = 1 << 30
-    src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        zdo.device_copy(dst, src, stream)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(10):
-        zdo.device_copy(dst, src, stream)
-    c1.record(stream)
-    torch.cuda.synchronize(dev)
-    copy_gbps = 2 * nb / (c0.elapsed_time(c1) / 1e3 / 10) / 1e9
+    flush_src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(flush_src)
+    copy_s, _ = back_to_back(torch, lambda: zdo.device_copy(dst, flush_src, stream), stream, 10)
+    copy_gbps = 2 * nb / copy_s / 1e9
+    del dst
     log(f"copy reference: {copy_gbps:.0f} GB/s")
 
-    # cold caches: the same step after 1 GiB of ordinary (temporal) reads,
-    # which evict the 256 MB Infinity Cache and the L2s as the forward/backward
-    # passes of a training step would. Reads, so that no dirty line of the
-    # flush is written back during the step; the copy above uses non-temporal
-    # accesses, which do not displace cached lines. HIP events around the step
-    # kernel only
-    n_cold = min(args.steps, 50)
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_cold)]
-    for a, b in kev:
-        src.sum()
-        t += 1
-        a.record(stream)
-        step(t)
-        b.record(stream)
-    torch.cuda.synchronize(dev)
-    cold_s = float(np.mean([a.elapsed_time(b) for a, b in kev])) / 1e3
-    cold = {"kernel_avg_us": cold_s * 1e6, "achieved_gbps": alg_bytes / cold_s / 1e9,
-            "frac": alg_bytes / cold_s / 1e9 / PEAK_HBM_GBPS, "elements_per_s": E / cold_s, "steps": n_cold,
-            "flush": "torch sum over a 1 GiB buffer (temporal loads) before every step, outside the kernel's "
-                     "events"}
-    log(f"cold caches: kernel avg {cold_s * 1e6:.1f} us, {cold['achieved_gbps']:.0f} GB/s algorithmic")
-    del src, dst
+    cold_s = cold(torch, np, lambda: sh.step(zdo, stream), stream, flush_src, min(args.steps, 20))
+    cold_r = rate(sh.alg_bytes, cold_s)
+    log(f"cold caches: kernel avg {cold_s * 1e6:.1f} us, {cold_r['gbps']:.0f} GB/s algorithmic")
 
-    variants = measure_variants(zdo, torch, np, plan, w, reps, coords, stream, min(args.steps, 50))
+    variants = None
+    if not args.no_variants:
+        variants = measure_variants(zdo, torch, np, plan, w, sh.reps, sh.coords, stream, min(args.steps, 20))
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(plan, w, reps, coords, master, exp_avg, exp_avg_sq, args.cpu_seconds)
+        cpu = cpu_baseline(torch, np, sh, args.cpu_seconds)
+
+    del sh
+    torch.cuda.synchronize(dev)
+    torch.cuda.empty_cache()
+    configs = {}
+    if args.configs == "all":
+        for name in ("tiny", "gpt2_small", "llama3_8b", "llama3_70b", "frag"):
+            if name == w.name:
+                continue
+            configs[name] = measure_config(zdo, torch, np, W, W.get(name), dev, stream, flush_src)
+            torch.cuda.synchronize(dev)
+            torch.cuda.empty_cache()
 
     traffic = traffic_from_profiles(w.name)
+    in_cache = 12 * plan.shard_numel <= STATE_CACHE_BYTES
     out = {
         "metric": METRIC,
-        "value": E / (ms_per_step / 1e3),
+        "value": E / wall_s,
         "unit": "elements/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -239,19 +293,19 @@ def main() -> int:
         "config": {
             "workload": w.name,
             "params": len(w.param_numel),
-            "buffer_elements": N,
+            "buffer_elements": plan.buffer_numel,
             "bucket_elements": w.bucket_numel,
             "buckets": int(plan.buckets().size),
             "dp_size": D,
             "rank": rank,
             "owned_elements": E,
-            "grad_replicas": f"{D} x bf16 {'whole buffers' if coords == zdo.WORLD else 'shard slices'}",
+            "grad_replicas": f"{D} x bf16 {'whole buffers' if sh_coords_world(w) else 'shard slices'}",
             "state": "fp32 master/exp_avg/exp_avg_sq shard",
-            "bytes_per_element": bytes_per_elem,
+            "bytes_per_element": 2 * D + 26,
             "buffer_stagger_bytes": args.stagger,
         },
-        "hbm_gbps": alg_bytes / (ms_per_step / 1e3) / 1e9,
-        "hbm_frac_of_peak": alg_bytes / (ms_per_step / 1e3) / 1e9 / PEAK_HBM_GBPS,
+        "hbm_gbps": E * (2 * D + 26) / wall_s / 1e9,
+        "hbm_frac_of_peak": E * (2 * D + 26) / wall_s / 1e9 / PEAK_HBM_GBPS,
         "roofline": {
             "bound": "hbm",
             "achieved": achieved,
@@ -260,24 +314,88 @@ def main() -> int:
             "frac": achieved / PEAK_HBM_GBPS,
             "traffic": traffic,
         },
-        "kernel": {"name": "step_kernel", "avg_us": kern_avg_s * 1e6,
+        "kernel": {"name": "step_kernel", "avg_us": kern_s * 1e6,
                    "how": "one HIP event pair around the timed steps on the launch stream, divided by the steps",
                    "single_launches": isolated,
-                   "source_sha256_16": kernel_source_hash()},
-        "cold_cache": cold,
-        "variants": variants,
+                   "source_sha256_16": kernel_source_hash(),
+                   "state_in_infinity_cache": in_cache},
+        "cold_cache": {"kernel_avg_us": cold_s * 1e6, "achieved_gbps": cold_r["gbps"], "frac": cold_r["frac"],
+                       "elements_per_s": E / cold_s,
+                       "flush": "torch sum over a 1 GiB buffer (temporal loads) before every step, outside the "
+                                "kernel's events"},
         "copy_reference_gbps": copy_gbps,
+        "variants": variants,
+        "configs": configs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
     return 0
 
 
+def sh_coords_world(w) -> bool:
+    return w.grad_mode == "world"
+
+
+# ---- every workload, rank by rank -----------------------------------------------------------------
+
+def measure_config(zdo, torch, np, W, w, dev, stream, flush_src) -> dict:
+    """Every rank the workload times: the step back to back and with cold
+    caches. HBM figure: cold caches where the rank's fp32 state fits in 1 GiB
+    (back-to-back steps there read part of it from the Infinity Cache),
+    back to back otherwise (the state streams from HBM either way)."""
+    t0 = time.perf_counter()
+    ranks = []
+    reps = None
+    big = None
+    for r in w.time_ranks:
+        sh = Shard(zdo, torch, W, w, r, dev, reps=reps)
+        if sh.coords == zdo.WORLD:
+            reps = sh.reps          # whole buffers: shared by every rank
+        small = sh.state_bytes <= STATE_CACHE_BYTES
+        n = 200 if small else 20
+        b2b, _ = back_to_back(torch, lambda: sh.step(zdo, stream), stream, n)
+        entry = {"rank": r, "owned_elements": sh.E, "bytes_per_element": sh.bytes_per_elem,
+                 "back_to_back": rate(sh.alg_bytes, b2b)}
+        if small:
+            c = cold(torch, np, lambda: sh.step(zdo, stream), stream, flush_src, 50)
+            entry["cold_cache"] = rate(sh.alg_bytes, c)
+            hbm = entry["cold_cache"]
+            entry["hbm_figure"] = "cold_cache"
+        else:
+            hbm = entry["back_to_back"]
+            entry["hbm_figure"] = "back_to_back (the state exceeds the Infinity Cache)"
+        entry["elements_per_s"] = sh.E / (hbm["us"] * 1e-6)
+        entry["frac"] = hbm["frac"]
+        ranks.append(entry)
+        big = sh
+        del sh
+    out = {"dp_size": w.dp_size, "grad_replicas": w.grad_mode, "ranks": ranks,
+           "hbm_frac_min": min(e["frac"] for e in ranks), "hbm_frac_max": max(e["frac"] for e in ranks)}
+    if w.name == "frag":
+        # the force_all_reduce path: the whole reduced buffer (2D + 2 bytes
+        # per buffer element), then the step on it as one pre-reduced
+        # contribution
+        Nn = big.plan.buffer_numel
+        full = torch.empty(Nn, dtype=torch.int16, device=dev)
+        fn = lambda: zdo.force_all_reduce(big.plan, reps, w.scale, full, stream)   # noqa: E731
+        b2b, _ = back_to_back(torch, fn, stream, 50)
+        c = cold(torch, np, fn, stream, flush_src, 20)
+        out["force_all_reduce"] = {"elements": Nn, "bytes_per_element": 2 * w.dp_size + 2,
+                                   "back_to_back": rate(Nn * (2 * w.dp_size + 2), b2b),
+                                   "cold_cache": rate(Nn * (2 * w.dp_size + 2), c)}
+        del full
+    del big, reps
+    log(f"config {w.name}: " + ", ".join(f"r{e['rank']} {e['frac']:.1%}" for e in ranks) +
+        f" ({time.perf_counter() - t0:.1f}s)")
+    return out
+
+
+# ---- the other calls on the headline shard --------------------------------------------------------
+
 def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> dict:
     """The other device calls on the same inputs: reduce_scatter_local over
     the rank's whole ranges (2D + 2 bytes per element of the ranges), the step
-    bucket by bucket, the clipped path, two instances (composed from a
-    reduce-scatter within each and the step on both results, and in one
+    bucket by bucket, the clipped path, two instances (composed and in one
     pass), the parameter all-gather in place (4 bytes per element of the
     other ranks' ranges) and, when the replicas are whole buffers,
     force_all_reduce over the padded buffer (2D + 2 bytes per buffer
@@ -289,16 +407,7 @@ def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> d
     out = {}
 
     def timed(fn) -> float:
-        """Average seconds per call of n back-to-back calls between one event pair."""
-        for _ in range(3):
-            fn()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(n):
-            fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / 1e3 / n
+        return back_to_back(torch, fn, stream, n)[0]
 
     ranges = int(sum(b["shard_numel"] for b in plan.buckets()))
     red = torch.empty(plan.shard_numel, dtype=torch.int16, device=reps[0].device)
@@ -309,12 +418,11 @@ def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> d
     log(f"reduce_scatter_local: {t * 1e6:.1f} us, {gbps:.0f} GB/s algorithmic")
     del red
     # bucket by bucket: the same step launched once per bucket, last bucket
-    # first (the order a backward pass makes them ready), in one timed region
+    # first (the order a backward pass makes them ready)
     nb = int(plan.buckets().size)
     st_b = [torch.zeros(plan.shard_numel, dtype=torch.float32, device=reps[0].device) for _ in range(3)]
     par_b = torch.empty(plan.extent(coords), dtype=torch.int16, device=reps[0].device)
-    hp_b = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, step=1)
-
+    hp_b = dict(w.hp, step=1)
     reps_b = zdo.Buffers(reps, "replicas")   # checked once for the nb launches
 
     def per_bucket(st=stream):
@@ -322,9 +430,7 @@ def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> d
             zdo.sharded_adam_step(plan, reps_b, coords, w.scale, *st_b, par_b, coords, stream=st,
                                   buckets=(b, b + 1), **hp_b)
     t_b = timed(per_bucket)
-    # the same launches replayed from a HIP graph, so that the host's
-    # per-launch cost (Python here) does not leave the GPU idle between
-    # short launches
+    # the same launches replayed from a HIP graph
     side = torch.cuda.Stream(device=reps[0].device)
     side.wait_stream(torch.cuda.current_stream(reps[0].device))
     with torch.cuda.stream(side):
@@ -355,7 +461,7 @@ def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> d
     red = torch.empty(plan.shard_numel, dtype=torch.int16, device=dev)
     st = [torch.zeros(plan.shard_numel, dtype=torch.float32, device=dev) for _ in range(3)]
     par = torch.empty(plan.extent(coords), dtype=torch.int16, device=dev)
-    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, step=1)
+    hp = dict(w.hp, step=1)
     r = plan.rank
     t_norm = timed(lambda: zdo.grad_norm_sq(plan, reps, coords, w.scale, ws, parts[r:r + 1], red, zdo.LOCAL,
                                             stream=stream))
@@ -371,8 +477,6 @@ def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> d
         "elements": E, "kernel_avg_us": t_pre * 1e6, "achieved_gbps": E * 28 / t_pre / 1e9,
         "frac": E * 28 / t_pre / 1e9 / PEAK_HBM_GBPS, "elements_per_s": E / t_pre}
     log(f"pre-reduced step (n_grads = 1): {t_pre * 1e6:.1f} us, {E * 28 / t_pre / 1e9:.0f} GB/s algorithmic")
-    # the write-back alone (bf16(master) into the owned elements): 4 + 2
-    # bytes per owned element
     t_wb = timed(lambda: zdo.writeback_params(plan, st[0], par, coords, stream=stream))
     out["writeback_params"] = {"bytes_per_element": 6, "elements": E, "kernel_avg_us": t_wb * 1e6,
                                "achieved_gbps": E * 6 / t_wb / 1e9, "frac": E * 6 / t_wb / 1e9 / PEAK_HBM_GBPS}
@@ -391,8 +495,7 @@ def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> d
 
     # two instances of D ranks: the bench's replicas and D more in the same
     # coordinates. Composed: a reduce-scatter within each instance, then the
-    # step on the two results with scale 1 (which sums them as the all-reduce
-    # across instances does). One pass: sharded_adam_step_instances.
+    # step on the two results with scale 1. One pass: sharded_adam_step_instances.
     n_inst = 2
     Ln = plan.shard_numel
     n_rep = plan.extent(coords)
@@ -430,17 +533,12 @@ def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> d
             "one_pass": {"path": "sharded_adam_step_instances", "bytes_per_element": 2 * n_inst * D + 26,
                          "kernel_avg_us": t_one * 1e6, "achieved_gbps": bytes_one / t_one / 1e9,
                          "frac": bytes_one / t_one / 1e9 / PEAK_HBM_GBPS, "elements_per_s": E / t_one}}
-        log(f"two-level, {n_inst} instances: composed rs {t_rs0 * 1e6:.1f} + {t_rs1 * 1e6:.1f} us + step "
-            f"{t_st * 1e6:.1f} us ({bytes_all / t_all / 1e9:.0f} GB/s); one pass {t_one * 1e6:.1f} us "
-            f"({bytes_one / t_one / 1e9:.0f} GB/s)")
+        log(f"two-level, {n_inst} instances: composed {t_all * 1e6:.1f} us ({bytes_all / t_all / 1e9:.0f} GB/s); "
+            f"one pass {t_one * 1e6:.1f} us ({bytes_one / t_one / 1e9:.0f} GB/s)")
         del extra, inst1, rs, st, par
 
-    # parameter all-gather, in place into this rank's buffer: the other ranks'
-    # ranges of every padded bucket copied from their buffers. Sources: the
-    # bench's whole-buffer replicas, else D uninitialised buffers of N if they
-    # fit (the copy's timing does not depend on the values)
+    # parameter all-gather, in place into this rank's buffer
     N = plan.buffer_numel
-    ranges = int(sum(b["shard_numel"] for b in plan.buckets()))
     srcs = None
     if coords == zdo.WORLD:
         srcs = list(reps)
@@ -462,7 +560,6 @@ def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> d
     del srcs
 
     if coords == zdo.WORLD:
-        N = plan.buffer_numel
         full = torch.empty(N, dtype=torch.int16, device=reps[0].device)
         t = timed(lambda: zdo.force_all_reduce(plan, reps, w.scale, full, stream))
         gbps = N * (2 * D + 2) / t / 1e9
@@ -473,37 +570,84 @@ def measure_variants(zdo, torch, np, plan, w, reps, coords, stream, n: int) -> d
     return out
 
 
-def cpu_baseline(plan, w, reps, coords, master, exp_avg, exp_avg_sq, seconds: float) -> dict:
-    """The oracle (oracle/step.c through oracle.step.rank_step) on the host
-    cores, over the same rank's whole shard, repeated for about `seconds`;
-    only the step compute is timed."""
-    import numpy as np
+# ---- the oracle on the host -------------------------------------------------------------------------
 
+def cpu_baseline(torch, np, sh, seconds: float) -> dict:
+    """The oracle's element arithmetic (oracle/step.c) on the host cores,
+    streamed over the rank's owned elements in chunks of at most 2^26 slots
+    as the oracle's range map gives them (one run per bucket): each chunk's D
+    contribution slices and state are copied to pinned host memory, then one
+    timed oracle step runs on them. Chunks spread evenly over the shard are
+    taken until about `seconds` of oracle compute (a bounded sample unless
+    the whole shard fits in that time); only the oracle's compute is timed.
+    The same on one core over one chunk of at most 2^22 slots."""
     import oracle.layout as OL
     import oracle.numerics as ON
-    import oracle.step as OS
 
-    t0 = time.perf_counter()
-    lay = OL.build_layout(w.param_numel, w.bucket_numel, w.dp_size)
-    r = plan.rank
-    reps_h = [x.cpu().numpy().view(np.uint16) for x in reps]
-    st = [x.cpu().numpy().copy() for x in (master, exp_avg, exp_avg_sq)]
-    par = np.zeros(reps_h[0].size, np.uint16)
-    log(f"cpu baseline: host copies in {time.perf_counter() - t0:.1f}s, {ON.threads()} threads")
-    passes, spent, t = 0, 0.0, 0
-    while spent < seconds or passes < 1:
-        t += 1
-        hp = ON.hp_array(w.hp, t)
+    w, r, D = sh.w, sh.rank, sh.D
+    lay = OL.build_layout(w.param_numel, w.bucket_numel, D)
+    runs = []
+    for pc in OL.rank_pieces(lay, r):
+        if runs and runs[-1][0] + runs[-1][2] == pc.shard_offset and \
+                runs[-1][1] + runs[-1][2] == pc.gbuf_world.start:
+            runs[-1][2] += pc.gbuf_world.size
+        else:
+            runs.append([pc.shard_offset, pc.gbuf_world.start, pc.gbuf_world.size])
+    world = sh.coords == 0
+    chunks = [(k + off, (wb if world else k) + off, min(CPU_CHUNK, n - off))
+              for k, wb, n in runs for off in range(0, n, CPU_CHUNK)]
+    cmax = max(c[2] for c in chunks)
+    stage_g = torch.empty((D, cmax), dtype=torch.int16, pin_memory=True)
+    stage_s = torch.empty((3, cmax), dtype=torch.float32, pin_memory=True)
+    hp = ON.hp_array(w.hp, 1)
+    cores = ON.threads()
+
+    def load(k0, gi, n):
+        for j in range(D):
+            stage_g[j, :n].copy_(sh.reps[j][gi:gi + n], non_blocking=True)
+        for i in range(3):
+            stage_s[i, :n].copy_(sh.state[i][k0:k0 + n], non_blocking=True)
+        torch.cuda.synchronize()
+        return [stage_g[j, :n].numpy().view(np.uint16) for j in range(D)], [stage_s[i, :n].numpy() for i in range(3)]
+
+    # chunks in an order that spreads any prefix of them over the shard
+    order = sorted(range(len(chunks)), key=lambda i: (bin(i)[2:].zfill(32)[::-1], i))
+    done = spent = 0.0
+    taken = 0
+    par = np.empty(cmax, np.uint16)
+    t_all = time.perf_counter()
+    for i in order:
+        k0, gi, n = chunks[i]
+        grads, st = load(k0, gi, n)
         a = time.perf_counter()
-        OS.rank_step(lay, r, reps_h, coords, w.scale, *st, hp, par, coords)
+        ON.step(grads, w.scale, *st, hp, par[:n])
         spent += time.perf_counter() - a
-        passes += 1
-    E = plan.owned_numel
-    log(f"cpu baseline: {passes} passes in {spent:.1f}s")
-    return {"value": E * passes / spent, "unit": "elements/s", "cores": ON.threads(), "kind": "oracle",
-            "sample": f"rank {r}'s whole shard of {w.name} ({E} elements, D={w.dp_size}), {passes} passes, "
-                      f"{spent:.1f} s of step compute (host copies excluded)",
-            "gbps": E * (2 * w.dp_size + 26) * passes / spent / 1e9}
+        done += n
+        taken += 1
+        if spent >= seconds:
+            break
+    # one core, one chunk of at most 2^22 slots
+    k0, gi, n = chunks[order[0]]
+    n1 = min(n, 1 << 22)
+    grads, st = load(k0, gi, n1)
+    ON.set_threads(1)
+    a = time.perf_counter()
+    ON.step(grads, w.scale, *st, hp, par[:n1])
+    one = time.perf_counter() - a
+    ON.set_threads(cores)
+    E = sh.E
+    bpe = 2 * D + 26
+    log(f"cpu baseline: {int(done)} of {E} elements in {spent:.1f}s of oracle compute on {cores} threads "
+        f"({done / spent / 1e9:.3f} G elem/s); 1 core {n1 / one / 1e9:.4f} G elem/s; "
+        f"{time.perf_counter() - t_all:.1f}s with the host copies")
+    return {"value": done / spent, "unit": "elements/s", "cores": cores, "kind": "oracle",
+            "sample": f"rank {r}'s shard of {w.name} (D={D}): {taken} of {len(chunks)} chunks of at most 2^26 "
+                      f"slots, spread over the shard ({int(done)} of {E} owned elements, {done / E:.0%}), "
+                      f"{spent:.1f} s of oracle compute (host copies excluded)",
+            "gbps": done * bpe / spent / 1e9,
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+            "one_core": {"value": n1 / one, "unit": "elements/s", "elements": n1, "seconds": one}}
 
 
 if __name__ == "__main__":

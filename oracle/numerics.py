@@ -30,6 +30,8 @@ def load(path: str):
     L.oracle_bias_correction.restype = f32
     L.oracle_threads.argtypes = []
     L.oracle_threads.restype = ctypes.c_int
+    L.oracle_set_threads.argtypes = [ctypes.c_int]
+    L.oracle_set_threads.restype = None
     L.oracle_narrow.argtypes = [vp, i64, vp]
     L.oracle_widen.argtypes = [vp, i64, vp]
     L.oracle_reduce.argtypes = [i32, vp, f32, i64, vp]
@@ -61,6 +63,11 @@ def _check(a, dtype, n=None):
 
 def threads() -> int:
     return lib().oracle_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads of the element loops from now on (results do not depend on it)."""
+    lib().oracle_set_threads(int(n))
 
 
 def bias_correction(beta: float, t: int) -> float:

@@ -147,6 +147,18 @@ int oracle_threads(void)
 #endif
 }
 
+/* Threads for the element loops that follow (n >= 1); each element is
+ * independent, so results do not depend on it. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 void oracle_narrow(const float *x, int64_t n, uint16_t *out)
 {
     for (int64_t i = 0; i < n; ++i)

@@ -300,6 +300,24 @@ int grad_norm_sq(const zdo_plan *plan, const uint16_t *const *replicas, int32_t 
                  int32_t replica_coords, float scale, uint16_t *reduced_out, int32_t out_coords,
                  void *workspace, double *norm_sq_out, void *stream);
 
+/* grad_norm_sq without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. The per-tile partials go to a static
+ * device array of the library, ZDO_NO_ALLOC_SCRATCH_BYTES bytes on each GPU
+ * it runs on (held until the process ends); the call itself allocates
+ * nothing. Same kernels, same fixed summation order, so the results equal
+ * grad_norm_sq's bit for bit. The plan's zdo_plan_norm_workspace_bytes must
+ * not exceed ZDO_NO_ALLOC_SCRATCH_BYTES (64 MiB: up to 8,387,584 tiles of 512
+ * owned elements, about 4.29e9 elements per rank), else ZDO_EINVAL before
+ * anything is enqueued. Every call on one GPU uses that GPU's one array:
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * and give wrong results; calls ordered on one stream are safe. Other
+ * arguments and rules as grad_norm_sq. */
+#define ZDO_NO_ALLOC_SCRATCH_BYTES (64u << 20)
+int grad_norm_sq_no_alloc(const zdo_plan *plan, const uint16_t *const *replicas, int32_t n_replicas,
+                          int32_t replica_coords, float scale, uint16_t *reduced_out, int32_t out_coords,
+                          double *norm_sq_out, void *stream);
+
 /* From n_parts squared norms (device doubles, e.g. every rank's grad_norm_sq),
  * summed in index order in fp64: norm = sqrt(total) and the clipping
  * coefficient min(1, max_norm / (norm + 1e-6)) computed in fp64 and rounded to

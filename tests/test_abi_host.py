@@ -27,7 +27,7 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     L = Z.require_library()
     names = header_functions()
-    assert len(names) == 28, names
+    assert len(names) == 29, names
     assert sorted(Z.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -64,6 +64,28 @@ def test_short_plan_names_equal_the_prefixed_ones():
     finally:
         L.plan_destroy(h)
     L.plan_destroy(None)
+
+
+def test_no_alloc_norm_refuses_a_plan_beyond_its_scratch_before_anything_else():
+    """A rank whose norm needs more than the static scratch array
+    (ZDO_NO_ALLOC_SCRATCH_BYTES) is refused with EINVAL by the size check,
+    which comes before every device check: the replica list is NULL here, so
+    any other order would answer with a different message."""
+    L = Z.require_library()
+    sizes = np.array([(1 << 32) + (1 << 20)], dtype=np.int64)      # 2^32 + 2^20 elements, D = 1
+    h = ctypes.c_void_p()
+    assert L.build_range_map(sizes.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), 1, 1 << 40, 1, 0,
+                             ctypes.byref(h)) == 0
+    try:
+        need = L.zdo_plan_norm_workspace_bytes(h)
+        assert need > Z.NO_ALLOC_SCRATCH_BYTES
+        out = ctypes.c_double()
+        rc = L.grad_norm_sq_no_alloc(h, None, 1, Z.LOCAL, 1.0, None, Z.LOCAL, ctypes.byref(out), None)
+        assert rc == Z.EINVAL
+        assert b"scratch" in L.zdo_last_error()
+        assert L.grad_norm_sq_no_alloc(None, None, 1, Z.LOCAL, 1.0, None, Z.LOCAL, None, None) == Z.EINVAL
+    finally:
+        L.zdo_plan_destroy(h)
 
 
 def test_struct_layouts():

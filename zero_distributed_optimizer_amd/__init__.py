@@ -69,7 +69,9 @@ EXPORTS = ("build_range_map", "zdo_plan_destroy", "zdo_plan_buffer_numel", "zdo_
            "writeback_params", "reduce_scatter_local_buckets", "sharded_adam_step_buckets",
            "zdo_plan_norm_workspace_bytes", "grad_norm_sq", "clip_coefficient", "sharded_adam_step_clipped",
            "sharded_adam_step_instances", "all_gather_params", "zdo_device_copy", "zdo_last_error",
-           "plan_buckets", "plan_pieces", "plan_buffer_numel", "plan_shard_numel", "plan_destroy")
+           "plan_buckets", "plan_pieces", "plan_buffer_numel", "plan_shard_numel", "plan_destroy",
+           "grad_norm_sq_no_alloc")
+NO_ALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -112,6 +114,7 @@ def require_library() -> ctypes.CDLL:
     L.zdo_plan_norm_workspace_bytes.argtypes = [vp]
     L.zdo_plan_norm_workspace_bytes.restype = i64
     L.grad_norm_sq.argtypes = [vp, vp, i32, i32, f32, vp, i32, vp, vp, vp]
+    L.grad_norm_sq_no_alloc.argtypes = [vp, vp, i32, i32, f32, vp, i32, vp, vp]
     L.clip_coefficient.argtypes = [vp, i32, f32, vp, vp, vp]
     L.sharded_adam_step_clipped.argtypes = [vp, vp, i32, i32, f32, vp, vp, vp, vp, i32, ctypes.POINTER(Adam),
                                             vp, vp, vp]
@@ -123,7 +126,8 @@ def require_library() -> ctypes.CDLL:
     L.zdo_last_error.restype = ctypes.c_char_p
     for f in ("build_range_map", "zdo_plan_buckets", "zdo_plan_pieces", "plan_buckets", "plan_pieces",
               "reduce_scatter_local",
-              "force_all_reduce", "sharded_adam_step", "writeback_params", "grad_norm_sq", "clip_coefficient",
+              "force_all_reduce", "sharded_adam_step", "writeback_params", "grad_norm_sq", "grad_norm_sq_no_alloc",
+              "clip_coefficient",
               "sharded_adam_step_clipped", "reduce_scatter_local_buckets", "sharded_adam_step_buckets",
               "sharded_adam_step_instances", "all_gather_params", "zdo_device_copy"):
         getattr(L, f).restype = ctypes.c_int
@@ -392,6 +396,18 @@ def grad_norm_sq(plan: Plan, replicas, replica_coords: int, scale: float, worksp
     ro = None if reduced_out is None else _dev_ptr(reduced_out, "reduced_out", "bf16", plan.extent(out_coords))
     _check(require_library().grad_norm_sq(plan.handle, reps, len(replicas), replica_coords, scale, ro, out_coords,
                                           ws, ns, _stream(stream, norm_sq_out.device)))
+
+
+def grad_norm_sq_no_alloc(plan: Plan, replicas, replica_coords: int, scale: float, norm_sq_out,
+                          reduced_out=None, out_coords: int = WORLD, stream=None) -> None:
+    """grad_norm_sq with the library's static scratch array instead of a
+    workspace (for callers that cannot allocate); calls that overlap in time
+    on one GPU race."""
+    reps = _ptr_list(replicas, "replicas", plan.extent(replica_coords))
+    ns = _dev_ptr(norm_sq_out, "norm_sq_out", "f64", 1)
+    ro = None if reduced_out is None else _dev_ptr(reduced_out, "reduced_out", "bf16", plan.extent(out_coords))
+    _check(require_library().grad_norm_sq_no_alloc(plan.handle, reps, len(replicas), replica_coords, scale, ro,
+                                                   out_coords, ns, _stream(stream, norm_sq_out.device)))
 
 
 def clip_coefficient(norm_sq_parts, max_norm: float, coeff_out, norm_out=None, stream=None) -> None:

@@ -456,12 +456,9 @@ int64_t zdo_plan_norm_workspace_bytes(const zdo_plan *p) {
     return (p->param_tiles + 1024) * int64_t(sizeof(double));
 }
 
-int grad_norm_sq(const zdo_plan *plan, const uint16_t *const *replicas, int32_t n_replicas, int32_t replica_coords,
-                 float scale, uint16_t *reduced_out, int32_t out_coords, void *workspace, double *norm_sq_out,
-                 void *stream) {
-    const char *fn = "grad_norm_sq";
-    if (int rc = check_plan(plan, fn))
-        return rc;
+static int norm_sq_impl(const char *fn, const zdo_plan *plan, const uint16_t *const *replicas, int32_t n_replicas,
+                        int32_t replica_coords, float scale, uint16_t *reduced_out, int32_t out_coords,
+                        void *workspace, double *norm_sq_out, void *stream) {
     if (n_replicas < 1 || n_replicas > ZDO_MAX_REPLICAS)
         return fail(ZDO_EINVAL, std::string(fn) + ": n_replicas must be in [1, " + std::to_string(ZDO_MAX_REPLICAS) +
                                     "]");
@@ -508,6 +505,39 @@ int grad_norm_sq(const zdo_plan *plan, const uint16_t *const *replicas, int32_t 
     a.out = reduced_out;
     a.partial = static_cast<double *>(workspace);
     return launch_result(launch_norm(a, norm_sq_out, plan->lds_per_cu, static_cast<hipStream_t>(stream)), fn);
+}
+
+int grad_norm_sq(const zdo_plan *plan, const uint16_t *const *replicas, int32_t n_replicas, int32_t replica_coords,
+                 float scale, uint16_t *reduced_out, int32_t out_coords, void *workspace, double *norm_sq_out,
+                 void *stream) {
+    const char *fn = "grad_norm_sq";
+    if (int rc = check_plan(plan, fn))
+        return rc;
+    return norm_sq_impl(fn, plan, replicas, n_replicas, replica_coords, scale, reduced_out, out_coords, workspace,
+                        norm_sq_out, stream);
+}
+
+int grad_norm_sq_no_alloc(const zdo_plan *plan, const uint16_t *const *replicas, int32_t n_replicas,
+                          int32_t replica_coords, float scale, uint16_t *reduced_out, int32_t out_coords,
+                          double *norm_sq_out, void *stream) {
+    const char *fn = "grad_norm_sq_no_alloc";
+    if (!plan)
+        return fail(ZDO_EINVAL, std::string(fn) + ": plan is NULL");
+    // the size limit first: it needs only the plan's host tables
+    const int64_t need = zdo_plan_norm_workspace_bytes(plan);
+    if (need > int64_t(ZDO_NO_ALLOC_SCRATCH_BYTES))
+        return fail(ZDO_EINVAL, std::string(fn) + ": the plan needs " + std::to_string(need) +
+                                    " bytes of scratch, more than the library's static " +
+                                    std::to_string(ZDO_NO_ALLOC_SCRATCH_BYTES) +
+                                    " (use grad_norm_sq with a workspace of zdo_plan_norm_workspace_bytes)");
+    if (int rc = check_plan(plan, fn))
+        return rc;
+    void *scratch = nullptr;
+    const hipError_t e = no_alloc_scratch(&scratch);
+    if (e != hipSuccess)
+        return fail(ZDO_EHIP, std::string(fn) + ": the static scratch array's address: " + hipGetErrorString(e));
+    return norm_sq_impl(fn, plan, replicas, n_replicas, replica_coords, scale, reduced_out, out_coords, scratch,
+                        norm_sq_out, stream);
 }
 
 int clip_coefficient(const double *norm_sq_parts, int32_t n_parts, float max_norm, float *coeff_out,

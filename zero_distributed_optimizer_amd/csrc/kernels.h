@@ -98,5 +98,8 @@ hipError_t launch_gather(const GatherArgs &a, int lds_per_cu, hipStream_t stream
 hipError_t launch_norm(const NormArgs &a, double *norm_sq, int lds_per_cu, hipStream_t stream);
 hipError_t launch_clip(const double *parts, int32_t n, float max_norm, float *coeff, double *norm_out,
                        hipStream_t stream);
+// Device address of the library's static scratch array on the current
+// device (ZDO_NO_ALLOC_SCRATCH_BYTES bytes), looked up once per device.
+hipError_t no_alloc_scratch(void **out);
 
 }  // namespace zdo

@@ -27,9 +27,19 @@
 // for bit; the order of operations is the one stated in include/zdo.h.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 #pragma clang fp contract(off)
+
+// Scratch memory of grad_norm_sq_no_alloc: the squared norm's per-tile
+// partials and level sums for callers that cannot allocate. One copy per GPU
+// the library runs on, held until the process ends; every call on a GPU
+// shares it (calls that overlap in time on one GPU race). Host code never
+// names it: it takes the device address from hipGetSymbolAddress, per device
+// (zdo::no_alloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[ZDO_NO_ALLOC_SCRATCH_BYTES];
 
 namespace zdo {
 namespace {
@@ -868,6 +878,34 @@ hipError_t launch_norm(const NormArgs &a, double *norm_sq, int lds_per_cu, hipSt
     hipLaunchKernelGGL(tile_sum_kernel, dim3(unsigned(g)), dim3(kSumThreads), 0, stream, a.partial, n, chunk, level);
     hipLaunchKernelGGL(level_sum_kernel, dim3(1), dim3(kSumThreads), 0, stream, level, g, norm_sq);
     return hipGetLastError();
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each device, once looked up
+}  // namespace
+
+hipError_t no_alloc_scratch(void **out) {
+    *out = nullptr;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (!p)
+            return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_clip(const double *parts, int32_t n, float max_norm, float *coeff, double *norm_out,

@@ -372,9 +372,9 @@ def measure_config(zdo, torch, np, W, w, dev, stream, flush_src) -> dict:
     out = {"dp_size": w.dp_size, "grad_replicas": w.grad_mode, "ranks": ranks,
            "hbm_frac_min": min(e["frac"] for e in ranks), "hbm_frac_max": max(e["frac"] for e in ranks)}
     if w.name == "frag":
+        out["bucket_groups"] = bucket_groups(zdo, torch, big, stream, 100)
         # the force_all_reduce path: the whole reduced buffer (2D + 2 bytes
-        # per buffer element), then the step on it as one pre-reduced
-        # contribution
+        # per buffer element)
         Nn = big.plan.buffer_numel
         full = torch.empty(Nn, dtype=torch.int16, device=dev)
         fn = lambda: zdo.force_all_reduce(big.plan, reps, w.scale, full, stream)   # noqa: E731
@@ -387,6 +387,41 @@ def measure_config(zdo, torch, np, W, w, dev, stream, flush_src) -> dict:
     del big, reps
     log(f"config {w.name}: " + ", ".join(f"r{e['rank']} {e['frac']:.1%}" for e in ranks) +
         f" ({time.perf_counter() - t0:.1f}s)")
+    return out
+
+
+def bucket_groups(zdo, torch, sh, stream, n: int) -> dict:
+    """The step bucket by bucket, in bucket groups and in one launch, back to
+    back (n rounds each): one launch per bucket; three groups of adjacent
+    buckets (one launch each); three groups of scattered buckets (every third
+    bucket, one bucket-list launch each); the whole step."""
+    nb = int(sh.plan.buckets().size)
+    reps = zdo.Buffers(sh.reps, "replicas")
+    w = sh.w
+
+    def calls(groups):
+        def fn():
+            sh.t += 1
+            for g in groups:
+                zdo.sharded_adam_step(sh.plan, reps, sh.coords, w.scale, *sh.state, sh.params, sh.coords,
+                                      step=sh.t, stream=stream, buckets=g, **w.hp)
+        return fn
+    third = -(-nb // 3)
+    forms = {
+        "one_launch": [(0, nb)],
+        "per_bucket": [(b, b + 1) for b in reversed(range(nb))],
+        "three_adjacent_groups": [(k, min(nb, k + third)) for k in reversed(range(0, nb, third))],
+        "three_scattered_groups": [[(b, b + 1) for b in range(k, nb, 3)] for k in range(3)],
+    }
+    out = {"buckets": nb}
+    for name, groups in forms.items():
+        t, _ = back_to_back(torch, calls(groups), stream, n)
+        out[name] = {"launches": len(groups), "us": t * 1e6, "gbps": sh.alg_bytes / t / 1e9}
+    base = out["one_launch"]["us"]
+    for name in forms:
+        out[name]["vs_one_launch"] = out[name]["us"] / base
+    log("bucket groups: " + ", ".join(f"{k} {v['us']:.1f} us ({v['vs_one_launch']:.2f}x)"
+                                      for k, v in out.items() if isinstance(v, dict)))
     return out
 
 

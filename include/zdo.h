@@ -264,6 +264,23 @@ int sharded_adam_step_buckets(const zdo_plan *plan, int32_t bucket_begin, int32_
                               float *master, float *exp_avg, float *exp_avg_sq, uint16_t *param_out,
                               int32_t param_coords, const zdo_adam *hp, float *main_grad_out, void *stream);
 
+/* The same two calls for several bucket ranges at once, in one launch (page
+ * 1, §4.2: the buckets of a group are handled together, their communication
+ * coalesced into one kernel). bucket_ranges: host array of n_ranges
+ * (begin, end) pairs, each with 0 <= begin <= end <= number of buckets,
+ * pairwise disjoint (overlap: ZDO_EINVAL), in any order; empty ranges are
+ * skipped and ranges that touch are merged. One launch covers up to 16
+ * disjoint runs of tiles; longer lists take one launch per 16 runs. The
+ * results equal the per-range calls bit for bit. n_ranges = 0 does
+ * nothing. Other arguments and rules as the full calls. */
+int reduce_scatter_local_bucket_list(const zdo_plan *plan, const int32_t *bucket_ranges, int32_t n_ranges,
+                                     const uint16_t *const *replicas, int32_t n_replicas, int32_t replica_coords,
+                                     float scale, uint16_t *out, int32_t out_coords, void *stream);
+int sharded_adam_step_bucket_list(const zdo_plan *plan, const int32_t *bucket_ranges, int32_t n_ranges,
+                                  const uint16_t *const *grads, int32_t n_grads, int32_t grad_coords, float scale,
+                                  float *master, float *exp_avg, float *exp_avg_sq, uint16_t *param_out,
+                                  int32_t param_coords, const zdo_adam *hp, float *main_grad_out, void *stream);
+
 /* ---- global-norm clipping ---------------------------------------------------
  * The distributed-training notes, §8.3: each rank's squared gradient sum is
  * all-reduced into the global norm sqrt(sum_i ||g_i||^2), and the gradients

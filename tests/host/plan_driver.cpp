@@ -17,6 +17,7 @@ hipError_t launch_copy(void *, const void *, int64_t, hipStream_t) { return hipE
 hipError_t launch_norm(const NormArgs &, double *, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_clip(const double *, int32_t, float, float *, double *, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_gather(const GatherArgs &, int, hipStream_t) { return hipErrorNoDevice; }
+hipError_t no_alloc_scratch(void **out) { *out = nullptr; return hipErrorNoDevice; }
 }
 
 int main() {
@@ -55,6 +56,13 @@ int main() {
         if (reduce_scatter_local(p, reps, D, ZDO_WORLD, 1.0f, nullptr, ZDO_WORLD, nullptr) == ZDO_OK) return 6;
         if (sharded_adam_step(p, reps, D, ZDO_WORLD, 1.0f, nullptr, nullptr, nullptr, nullptr, 0, &hp, nullptr, nullptr) == ZDO_OK) return 7;
         if (all_gather_params(p, reps, D, nullptr, nullptr) == ZDO_OK) return 8;
+        const int32_t ranges[4] = {0, nb, nb, nb};
+        if (sharded_adam_step_bucket_list(p, ranges, 2, reps, D, ZDO_WORLD, 1.0f, nullptr, nullptr, nullptr, nullptr, 0,
+                                          &hp, nullptr, nullptr) == ZDO_OK) return 13;
+        if (reduce_scatter_local_bucket_list(p, ranges, 2, reps, D, ZDO_WORLD, 1.0f, nullptr, ZDO_WORLD, nullptr) == ZDO_OK)
+            return 14;
+        double nsq = 0.0;
+        if (grad_norm_sq_no_alloc(p, reps, D, ZDO_WORLD, 1.0f, nullptr, ZDO_WORLD, &nsq, nullptr) == ZDO_OK) return 15;
         (void)zdo_last_error();
         zdo_plan_destroy(p);
     }

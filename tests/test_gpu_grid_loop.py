@@ -137,6 +137,21 @@ def test_bucket_ranges_and_instances_beyond_the_grid(loop_gpu):
     for g, wv, nm in zip(st, want, ("master", "exp_avg", "exp_avg_sq")):
         assert_f32(host_f32(g), wv, f"per bucket {nm}")
     assert_bf16(host_u16(par), want_par, "per bucket params")
+    # bucket lists: separate runs of tiles in one launch, each walked
+    # through the grid-stride continuation
+    st = [to_dev(x) for x in st0]
+    par = torch.full((N,), SENTINEL, dtype=torch.int16, device=DEV)
+    red = torch.full((N,), SENTINEL, dtype=torch.int16, device=DEV)
+    for g in ([(3, 4), (0, 1)], [(1, 3)]):
+        loop_gpu.sharded_adam_step(plan, reps_d[:D], loop_gpu.WORLD, scale, *st, par, loop_gpu.WORLD, buckets=g,
+                                   **hp_kwargs(hp, 3))
+        loop_gpu.reduce_scatter_local(plan, reps_d[:D], loop_gpu.WORLD, scale, red, loop_gpu.WORLD, buckets=g)
+    for g, wv, nm in zip(st, want, ("master", "exp_avg", "exp_avg_sq")):
+        assert_f32(host_f32(g), wv, f"bucket lists {nm}")
+    assert_bf16(host_u16(par), want_par, "bucket lists params")
+    want_rs = np.full(N, SENTINEL, np.uint16)
+    OS.reduce_scatter(lay, r, reps_h[:D], OS.WORLD, scale, want_rs, OS.WORLD)
+    assert_bf16(host_u16(red), want_rs, "bucket lists reduce-scatter")
     # two instances in one pass = reduce-scatter per instance, then the step
     # on the instance results
     st = [to_dev(x) for x in st0]

@@ -906,3 +906,86 @@ def test_buffers_off_the_cache_line(gpu, off_bytes):
     OS.all_gather(lay, bufs_h, want_g)
     assert_bf16(host_u16(bufs[r]), want_g, "all-gather")
     free()
+
+
+@pytest.mark.parametrize("name", ["frag", "many"])
+def test_bucket_lists(gpu, name):
+    """Page 1, §4.2: several bucket ranges ready together go in one launch
+    (sharded_adam_step_bucket_list, reduce_scatter_local_bucket_list).
+    Groups of non-adjacent buckets, launched group by group in shuffled
+    order, equal the full call and the oracle bit for bit; a list with more
+    than 16 separate runs (two launches) too; overlapping or out-of-range
+    lists are EINVAL and an empty list changes nothing."""
+    if name == "frag":
+        w = W.get("frag")
+        sizes, bucket, D, r = w.param_numel, w.bucket_numel, w.dp_size, 5
+        lay = OL.build_layout(sizes, bucket, D)
+        reps_d = _gen_world(w, lay.buffer_numel)
+        reps_h = [host_u16(x) for x in reps_d]
+    else:
+        rng = np.random.default_rng(78)
+        pr = random.Random(78)
+        sizes = [pr.choice([1, 7, 300, 2048, 5000]) for _ in range(120)]
+        bucket, D, r = 2000, 3, 2
+        lay = OL.build_layout(sizes, bucket, D)
+        reps_h = [bf16_host(rng, lay.buffer_numel) for _ in range(D)]
+        reps_d = [to_dev(x) for x in reps_h]
+    plan = gpu.build_range_map(sizes, bucket, D, r)
+    nb = len(lay.buckets)
+    N, Ln = plan.buffer_numel, plan.shard_numel
+    hp = W.get("tiny").hp
+    rng = np.random.default_rng(6)
+    st0 = [(rng.standard_normal(Ln) * 0.02).astype(np.float32), (rng.standard_normal(Ln) * 1e-3).astype(np.float32),
+           ((rng.standard_normal(Ln) * 1e-3) ** 2).astype(np.float32)]
+    scale = 1.0 / D
+    want_st = [x.copy() for x in st0]
+    want_par = np.full(N, SENTINEL, np.uint16)
+    OS.rank_step(lay, r, reps_h, OS.WORLD, scale, *want_st, ON.hp_array(hp, 2), want_par, OS.WORLD)
+    want_rs = np.full(N, SENTINEL, np.uint16)
+    OS.reduce_scatter(lay, r, reps_h, OS.WORLD, scale, want_rs, OS.WORLD)
+
+    def check(groups, what):
+        st = [to_dev(x) for x in st0]
+        par = torch.full((N,), SENTINEL, dtype=torch.int16, device=DEV)
+        out = torch.full((N,), SENTINEL, dtype=torch.int16, device=DEV)
+        for g in groups:
+            gpu.sharded_adam_step(plan, reps_d, gpu.WORLD, scale, *st, par, gpu.WORLD, buckets=g, **hp_kwargs(hp, 2))
+            gpu.reduce_scatter_local(plan, reps_d, gpu.WORLD, scale, out, gpu.WORLD, buckets=g)
+        for x, wv, nm in zip(st, want_st, ("master", "exp_avg", "exp_avg_sq")):
+            assert_f32(host_f32(x), wv, f"{name} {what} {nm}")
+        assert_bf16(host_u16(par), want_par, f"{name} {what} params")
+        assert_bf16(host_u16(out), want_rs, f"{name} {what} reduce-scatter")
+
+    # three groups of scattered single buckets and pairs, shuffled
+    pr = random.Random(9)
+    order = list(range(nb))
+    pr.shuffle(order)
+    groups = [[(b, b + 1) for b in order[k::3]] for k in range(3)]
+    pr.shuffle(groups)
+    check(groups, "three scattered groups")
+    # every other bucket, then the rest: more than 16 runs in one list when
+    # there are more than 32 buckets
+    evens = [(b, b + 1) for b in range(0, nb, 2)]
+    odds = [(b, b + 1) for b in range(1, nb, 2)][::-1]
+    if name == "many":
+        assert len(evens) > 16
+    check([evens, odds], "alternate buckets")
+    # one list covering everything (touching ranges merge into one run)
+    check([[(b, b + 1) for b in reversed(range(nb))]], "all buckets, touching")
+    # errors and the empty list
+    st = [to_dev(x) for x in st0]
+    par = torch.full((N,), SENTINEL, dtype=torch.int16, device=DEV)
+    for bad in ([(0, 2), (1, 3)], [(0, nb + 1)], [(2, 1)], [(-1, 1)]):
+        with pytest.raises(gpu.ZdoError) as e:
+            gpu.sharded_adam_step(plan, reps_d, gpu.WORLD, scale, *st, par, gpu.WORLD, buckets=bad,
+                                  **hp_kwargs(hp, 2))
+        assert e.value.code == gpu.EINVAL
+        with pytest.raises(gpu.ZdoError) as e:
+            gpu.reduce_scatter_local(plan, reps_d, gpu.WORLD, scale, par, gpu.WORLD, buckets=bad)
+        assert e.value.code == gpu.EINVAL
+    gpu.sharded_adam_step(plan, reps_d, gpu.WORLD, scale, *st, par, gpu.WORLD, buckets=[], **hp_kwargs(hp, 2))
+    gpu.sharded_adam_step(plan, reps_d, gpu.WORLD, scale, *st, par, gpu.WORLD, buckets=[(3, 3)], **hp_kwargs(hp, 2))
+    assert all(np.array_equal(host_f32(x).view(np.uint32), y.view(np.uint32)) for x, y in zip(st, st0))
+    assert (host_u16(par) == SENTINEL).all()
+    del reps_d
+    free()

@@ -70,7 +70,7 @@ EXPORTS = ("build_range_map", "zdo_plan_destroy", "zdo_plan_buffer_numel", "zdo_
            "zdo_plan_norm_workspace_bytes", "grad_norm_sq", "clip_coefficient", "sharded_adam_step_clipped",
            "sharded_adam_step_instances", "all_gather_params", "zdo_device_copy", "zdo_last_error",
            "plan_buckets", "plan_pieces", "plan_buffer_numel", "plan_shard_numel", "plan_destroy",
-           "grad_norm_sq_no_alloc")
+           "grad_norm_sq_no_alloc", "reduce_scatter_local_bucket_list", "sharded_adam_step_bucket_list")
 NO_ALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
@@ -109,6 +109,9 @@ def require_library() -> ctypes.CDLL:
     L.sharded_adam_step.argtypes = [vp, vp, i32, i32, f32, vp, vp, vp, vp, i32, ctypes.POINTER(Adam), vp, vp]
     L.writeback_params.argtypes = [vp, vp, vp, i32, vp]
     L.reduce_scatter_local_buckets.argtypes = [vp, i32, i32, vp, i32, i32, f32, vp, i32, vp]
+    L.reduce_scatter_local_bucket_list.argtypes = [vp, vp, i32, vp, i32, i32, f32, vp, i32, vp]
+    L.sharded_adam_step_bucket_list.argtypes = [vp, vp, i32, vp, i32, i32, f32, vp, vp, vp, vp, i32,
+                                                ctypes.POINTER(Adam), vp, vp]
     L.sharded_adam_step_buckets.argtypes = [vp, i32, i32, vp, i32, i32, f32, vp, vp, vp, vp, i32,
                                             ctypes.POINTER(Adam), vp, vp]
     L.zdo_plan_norm_workspace_bytes.argtypes = [vp]
@@ -129,7 +132,8 @@ def require_library() -> ctypes.CDLL:
               "force_all_reduce", "sharded_adam_step", "writeback_params", "grad_norm_sq", "grad_norm_sq_no_alloc",
               "clip_coefficient",
               "sharded_adam_step_clipped", "reduce_scatter_local_buckets", "sharded_adam_step_buckets",
-              "sharded_adam_step_instances", "all_gather_params", "zdo_device_copy"):
+              "sharded_adam_step_instances", "all_gather_params", "zdo_device_copy",
+              "reduce_scatter_local_bucket_list", "sharded_adam_step_bucket_list"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -288,17 +292,33 @@ def _stream(stream, device) -> int:
     return stream.cuda_stream
 
 
+def _bucket_list(buckets):
+    """A list of (begin, end) pairs as the C-ABI's int32 pair array, or None
+    for a single (begin, end) pair."""
+    if len(buckets) == 2 and all(isinstance(b, (int, np.integer)) for b in buckets):
+        return None
+    arr = np.ascontiguousarray(np.asarray([[int(b), int(e)] for b, e in buckets], dtype=np.int32).reshape(-1))
+    return arr
+
+
 def reduce_scatter_local(plan: Plan, replicas, replica_coords: int, scale: float, out, out_coords: int,
                          stream=None, buckets=None) -> None:
-    """buckets=(begin, end): only those buckets (reduce_scatter_local_buckets)."""
+    """buckets=(begin, end): only those buckets (reduce_scatter_local_buckets);
+    buckets=[(begin, end), ...]: those ranges in one launch
+    (reduce_scatter_local_bucket_list)."""
     reps = _ptr_list(replicas, "replicas", plan.extent(replica_coords))
     o = _dev_ptr(out, "out", "bf16", plan.extent(out_coords))
     L, st = require_library(), _stream(stream, out.device)
     if buckets is None:
         _check(L.reduce_scatter_local(plan.handle, reps, len(replicas), replica_coords, scale, o, out_coords, st))
-    else:
+        return
+    lst = _bucket_list(buckets)
+    if lst is None:
         _check(L.reduce_scatter_local_buckets(plan.handle, int(buckets[0]), int(buckets[1]), reps, len(replicas),
                                               replica_coords, scale, o, out_coords, st))
+    else:
+        _check(L.reduce_scatter_local_bucket_list(plan.handle, lst.ctypes.data, lst.size // 2, reps, len(replicas),
+                                                  replica_coords, scale, o, out_coords, st))
 
 
 def force_all_reduce(plan: Plan, replicas, scale: float, out_full, stream=None) -> None:
@@ -316,7 +336,9 @@ def sharded_adam_step(plan: Plan, grads, grad_coords: int, scale: float, master,
                       param_out=None, param_coords: int = WORLD, *, lr: float, beta1: float, beta2: float,
                       eps: float, weight_decay: float, step: int, main_grad_out=None, stream=None,
                       buckets=None) -> None:
-    """buckets=(begin, end): only those buckets (sharded_adam_step_buckets)."""
+    """buckets=(begin, end): only those buckets (sharded_adam_step_buckets);
+    buckets=[(begin, end), ...]: those ranges in one launch
+    (sharded_adam_step_bucket_list)."""
     L = plan.shard_numel
     g = _ptr_list(grads, "grads", plan.extent(grad_coords))
     m = _dev_ptr(master, "master", "f32", L)
@@ -329,9 +351,15 @@ def sharded_adam_step(plan: Plan, grads, grad_coords: int, scale: float, master,
     if buckets is None:
         _check(L.sharded_adam_step(plan.handle, g, len(grads), grad_coords, scale, m, a, s, p, param_coords,
                                    ctypes.byref(hp), mg, st))
-    else:
+        return
+    lst = _bucket_list(buckets)
+    if lst is None:
         _check(L.sharded_adam_step_buckets(plan.handle, int(buckets[0]), int(buckets[1]), g, len(grads),
                                            grad_coords, scale, m, a, s, p, param_coords, ctypes.byref(hp), mg, st))
+    else:
+        _check(L.sharded_adam_step_bucket_list(plan.handle, lst.ctypes.data, lst.size // 2, g, len(grads),
+                                               grad_coords, scale, m, a, s, p, param_coords, ctypes.byref(hp), mg,
+                                               st))
 
 
 def sharded_adam_step_clipped(plan: Plan, grads, grad_coords: int, scale: float, master, exp_avg, exp_avg_sq,

@@ -2,9 +2,12 @@
 // launches. Declared and documented in include/zdo.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <new>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "kernels.h"
 #include "zdo_internal.h"
@@ -149,6 +152,78 @@ int check_buckets(const zdo_plan *plan, int32_t b0, int32_t b1, const char *fn) 
     return ZDO_OK;
 }
 
+typedef std::pair<int32_t, int32_t> BucketRange;
+
+// n (begin, end) pairs: each within [0, number of buckets], pairwise
+// disjoint; sorted by begin into `out`, empty ranges dropped.
+int check_bucket_list(const zdo_plan *plan, const int32_t *pairs, int32_t n, const char *fn,
+                      std::vector<BucketRange> &out) {
+    if (n < 0 || (n > 0 && !pairs))
+        return fail(ZDO_EINVAL, std::string(fn) + ": need n_ranges >= 0 and a range array");
+    out.clear();
+    for (int32_t i = 0; i < n; ++i) {
+        if (int rc = check_buckets(plan, pairs[2 * i], pairs[2 * i + 1], fn))
+            return rc;
+        if (pairs[2 * i] < pairs[2 * i + 1])
+            out.emplace_back(pairs[2 * i], pairs[2 * i + 1]);
+    }
+    std::sort(out.begin(), out.end());
+    for (size_t i = 1; i < out.size(); ++i)
+        if (out[i].first < out[i - 1].second)
+            return fail(ZDO_EINVAL, std::string(fn) + ": bucket ranges [" + std::to_string(out[i - 1].first) + ", " +
+                                        std::to_string(out[i - 1].second) + ") and [" +
+                                        std::to_string(out[i].first) + ", " + std::to_string(out[i].second) +
+                                        ") overlap");
+    return ZDO_OK;
+}
+
+struct TileRun {
+    int64_t first, count;
+};
+
+// The tile runs of a launch space that cover sorted, disjoint bucket ranges;
+// runs that touch are merged and empty ones dropped.
+std::vector<TileRun> tile_runs(const std::vector<Seg> &segs, const int32_t *seg_bucket, int64_t total_tiles,
+                               const std::vector<BucketRange> &ranges) {
+    std::vector<TileRun> runs;
+    for (const BucketRange &b : ranges) {
+        int64_t first = 0, count = 0;
+        bucket_tiles(segs, seg_bucket, total_tiles, b.first, b.second, first, count);
+        if (count <= 0)
+            continue;
+        if (!runs.empty() && runs.back().first + runs.back().count == first)
+            runs.back().count += count;
+        else
+            runs.push_back({first, count});
+    }
+    return runs;
+}
+
+// Launch walks over the runs, up to kMaxTileRuns runs each; `launch` takes a
+// Walk and returns the launch's hipError_t.
+template <typename F>
+int launch_runs(const std::vector<TileRun> &runs, const Seg *segs, const GroupSeg *group, int64_t nseg,
+                const char *fn, F launch) {
+    for (size_t c = 0; c < runs.size(); c += kMaxTileRuns) {
+        Walk w{};
+        w.segs = segs;
+        w.group = group;
+        w.nseg = nseg;
+        const size_t n = std::min(runs.size() - c, size_t(kMaxTileRuns));
+        w.nruns = int32_t(n);
+        int64_t start = 0;
+        for (size_t r = 0; r < n; ++r) {
+            w.run_begin[r] = runs[c + r].first;
+            w.run_start[r] = start;
+            start += runs[c + r].count;
+        }
+        w.ntiles = start;
+        if (int rc = launch_result(launch(w), fn))
+            return rc;
+    }
+    return ZDO_OK;
+}
+
 }  // namespace
 
 void set_error(const std::string &msg) { g_error = msg; }
@@ -229,7 +304,7 @@ int64_t plan_buffer_numel(const zdo_plan *p) { return zdo_plan_buffer_numel(p); 
 int64_t plan_shard_numel(const zdo_plan *p) { return zdo_plan_shard_numel(p); }
 void plan_destroy(zdo_plan *p) { zdo_plan_destroy(p); }
 
-static int reduce_scatter_impl(const char *fn, const zdo_plan *plan, int32_t b0, int32_t b1,
+static int reduce_scatter_impl(const char *fn, const zdo_plan *plan, const std::vector<BucketRange> &ranges,
                                const uint16_t *const *replicas, int32_t n_replicas, int32_t replica_coords,
                                float scale, uint16_t *out, int32_t out_coords, void *stream) {
     if (n_replicas < 1 || n_replicas > ZDO_MAX_REPLICAS)
@@ -250,15 +325,21 @@ static int reduce_scatter_impl(const char *fn, const zdo_plan *plan, int32_t b0,
         if (overlap(so, spans[j]) && !(out == replicas[j] && out_coords == replica_coords))
             return fail(ZDO_EALIAS, std::string(fn) + ": out overlaps replica " + std::to_string(j) +
                                         " without coinciding with it");
-    int64_t first = 0, count = 0;
-    bucket_tiles(plan->range_segs, nullptr, plan->range_tiles, b0, b1, first, count);
-    a.walk = {plan->d_range_segs, plan->d_range_group, int64_t(plan->range_segs.size()), count, 0, first};
     a.nrep = n_replicas;
     a.in_local = replica_coords == ZDO_LOCAL;
     a.out_local = out_coords == ZDO_LOCAL;
     a.scale = scale;
     a.out = out;
-    return launch_result(launch_reduce(a, plan->lds_per_cu, static_cast<hipStream_t>(stream)), fn);
+    const std::vector<TileRun> runs = tile_runs(plan->range_segs, nullptr, plan->range_tiles, ranges);
+    return launch_runs(runs, plan->d_range_segs, plan->d_range_group, int64_t(plan->range_segs.size()), fn,
+                       [&](const Walk &w) {
+                           a.walk = w;
+                           return launch_reduce(a, plan->lds_per_cu, static_cast<hipStream_t>(stream));
+                       });
+}
+
+static std::vector<BucketRange> all_buckets(const zdo_plan *plan) {
+    return {BucketRange(0, int32_t(plan->buckets.size()))};
 }
 
 int reduce_scatter_local(const zdo_plan *plan, const uint16_t *const *replicas, int32_t n_replicas,
@@ -266,8 +347,8 @@ int reduce_scatter_local(const zdo_plan *plan, const uint16_t *const *replicas, 
     const char *fn = "reduce_scatter_local";
     if (int rc = check_plan(plan, fn))
         return rc;
-    return reduce_scatter_impl(fn, plan, 0, int32_t(plan->buckets.size()), replicas, n_replicas, replica_coords,
-                               scale, out, out_coords, stream);
+    return reduce_scatter_impl(fn, plan, all_buckets(plan), replicas, n_replicas, replica_coords, scale, out,
+                               out_coords, stream);
 }
 
 int reduce_scatter_local_buckets(const zdo_plan *plan, int32_t bucket_begin, int32_t bucket_end,
@@ -278,8 +359,21 @@ int reduce_scatter_local_buckets(const zdo_plan *plan, int32_t bucket_begin, int
         return rc;
     if (int rc = check_buckets(plan, bucket_begin, bucket_end, fn))
         return rc;
-    return reduce_scatter_impl(fn, plan, bucket_begin, bucket_end, replicas, n_replicas, replica_coords, scale, out,
-                               out_coords, stream);
+    return reduce_scatter_impl(fn, plan, {BucketRange(bucket_begin, bucket_end)}, replicas, n_replicas,
+                               replica_coords, scale, out, out_coords, stream);
+}
+
+int reduce_scatter_local_bucket_list(const zdo_plan *plan, const int32_t *bucket_ranges, int32_t n_ranges,
+                                     const uint16_t *const *replicas, int32_t n_replicas, int32_t replica_coords,
+                                     float scale, uint16_t *out, int32_t out_coords, void *stream) {
+    const char *fn = "reduce_scatter_local_bucket_list";
+    if (int rc = check_plan(plan, fn))
+        return rc;
+    std::vector<BucketRange> ranges;
+    if (int rc = check_bucket_list(plan, bucket_ranges, n_ranges, fn, ranges))
+        return rc;
+    return reduce_scatter_impl(fn, plan, ranges, replicas, n_replicas, replica_coords, scale, out, out_coords,
+                               stream);
 }
 
 int force_all_reduce(const zdo_plan *plan, const uint16_t *const *replicas, int32_t n_replicas, float scale,
@@ -301,7 +395,7 @@ int force_all_reduce(const zdo_plan *plan, const uint16_t *const *replicas, int3
         if (overlap(so, spans[j]) && out_full != replicas[j])
             return fail(ZDO_EALIAS, std::string(fn) + ": out_full overlaps replica " + std::to_string(j) +
                                         " without coinciding with it");
-    a.walk = {nullptr, nullptr, 0, seg_tiles(0, plan->buffer_numel), plan->buffer_numel, 0};
+    a.walk = one_run(nullptr, nullptr, 0, 0, seg_tiles(0, plan->buffer_numel), plan->buffer_numel);
     a.nrep = n_replicas;
     a.in_local = 0;
     a.out_local = 0;
@@ -312,16 +406,11 @@ int force_all_reduce(const zdo_plan *plan, const uint16_t *const *replicas, int3
 
 // n_instances groups of n_grads / n_instances contributions (1 for the plain
 // step).
-static int adam_step(const char *fn, const zdo_plan *plan, int32_t b0, int32_t b1, const uint16_t *const *grads,
-                     int32_t n_grads, int32_t n_instances, int32_t grad_coords, float scale, float *master,
-                     float *exp_avg, float *exp_avg_sq, uint16_t *param_out, int32_t param_coords,
-                     const zdo_adam *hp, const float *coeff, float *main_grad_out, void *stream) {
-    if (int rc = check_plan(plan, fn))
-        return rc;
-    if (b1 < 0)
-        b1 = int32_t(plan->buckets.size());
-    if (int rc = check_buckets(plan, b0, b1, fn))
-        return rc;
+static int adam_step(const char *fn, const zdo_plan *plan, const std::vector<BucketRange> &ranges,
+                     const uint16_t *const *grads, int32_t n_grads, int32_t n_instances, int32_t grad_coords,
+                     float scale, float *master, float *exp_avg, float *exp_avg_sq, uint16_t *param_out,
+                     int32_t param_coords, const zdo_adam *hp, const float *coeff, float *main_grad_out,
+                     void *stream) {
     if (n_grads < 1 || n_grads > ZDO_MAX_REPLICAS)
         return fail(ZDO_EINVAL, std::string(fn) + ": n_grads must be in [1, " + std::to_string(ZDO_MAX_REPLICAS) +
                                     "]");
@@ -380,9 +469,6 @@ static int adam_step(const char *fn, const zdo_plan *plan, int32_t b0, int32_t b
         if (coeff && overlap(written[i].s, span_of(coeff, 1, 4)))
             return fail(ZDO_EALIAS, std::string(fn) + ": " + written[i].name + " overlaps grad_coeff");
     }
-    int64_t first = 0, count = 0;
-    bucket_tiles(plan->param_segs, plan->param_seg_bucket.data(), plan->param_tiles, b0, b1, first, count);
-    a.walk = {plan->d_param_segs, plan->d_param_group, int64_t(plan->param_segs.size()), count, 0, first};
     a.nrep = n_grads;
     a.ninst = n_instances;
     a.dinst = n_grads / n_instances;
@@ -405,34 +491,63 @@ static int adam_step(const char *fn, const zdo_plan *plan, int32_t b0, int32_t b
     a.c.wd = hp->weight_decay;
     a.c.bc1 = bias_correction(hp->beta1, hp->step);
     a.c.bc2 = bias_correction(hp->beta2, hp->step);
-    return launch_result(launch_step(a, plan->lds_per_cu, static_cast<hipStream_t>(stream)), fn);
+    const std::vector<TileRun> runs = tile_runs(plan->param_segs, plan->param_seg_bucket.data(), plan->param_tiles,
+                                                ranges);
+    return launch_runs(runs, plan->d_param_segs, plan->d_param_group, int64_t(plan->param_segs.size()), fn,
+                       [&](const Walk &w) {
+                           a.walk = w;
+                           return launch_step(a, plan->lds_per_cu, static_cast<hipStream_t>(stream));
+                       });
 }
 
 int sharded_adam_step(const zdo_plan *plan, const uint16_t *const *grads, int32_t n_grads, int32_t grad_coords,
                       float scale, float *master, float *exp_avg, float *exp_avg_sq, uint16_t *param_out,
                       int32_t param_coords, const zdo_adam *hp, float *main_grad_out, void *stream) {
-    return adam_step("sharded_adam_step", plan, 0, -1, grads, n_grads, 1, grad_coords, scale, master, exp_avg,
-                     exp_avg_sq, param_out, param_coords, hp, nullptr, main_grad_out, stream);
+    const char *fn = "sharded_adam_step";
+    if (int rc = check_plan(plan, fn))
+        return rc;
+    return adam_step(fn, plan, all_buckets(plan), grads, n_grads, 1, grad_coords, scale, master, exp_avg, exp_avg_sq,
+                     param_out, param_coords, hp, nullptr, main_grad_out, stream);
 }
 
 int sharded_adam_step_buckets(const zdo_plan *plan, int32_t bucket_begin, int32_t bucket_end,
                               const uint16_t *const *grads, int32_t n_grads, int32_t grad_coords, float scale,
                               float *master, float *exp_avg, float *exp_avg_sq, uint16_t *param_out,
                               int32_t param_coords, const zdo_adam *hp, float *main_grad_out, void *stream) {
-    if (bucket_end < 0)
-        return fail(ZDO_EINVAL, "sharded_adam_step_buckets: bucket_end < 0");
-    return adam_step("sharded_adam_step_buckets", plan, bucket_begin, bucket_end, grads, n_grads, 1, grad_coords, scale,
-                     master, exp_avg, exp_avg_sq, param_out, param_coords, hp, nullptr, main_grad_out, stream);
+    const char *fn = "sharded_adam_step_buckets";
+    if (int rc = check_plan(plan, fn))
+        return rc;
+    if (int rc = check_buckets(plan, bucket_begin, bucket_end, fn))
+        return rc;
+    return adam_step(fn, plan, {BucketRange(bucket_begin, bucket_end)}, grads, n_grads, 1, grad_coords, scale, master,
+                     exp_avg, exp_avg_sq, param_out, param_coords, hp, nullptr, main_grad_out, stream);
+}
+
+int sharded_adam_step_bucket_list(const zdo_plan *plan, const int32_t *bucket_ranges, int32_t n_ranges,
+                                  const uint16_t *const *grads, int32_t n_grads, int32_t grad_coords, float scale,
+                                  float *master, float *exp_avg, float *exp_avg_sq, uint16_t *param_out,
+                                  int32_t param_coords, const zdo_adam *hp, float *main_grad_out, void *stream) {
+    const char *fn = "sharded_adam_step_bucket_list";
+    if (int rc = check_plan(plan, fn))
+        return rc;
+    std::vector<BucketRange> ranges;
+    if (int rc = check_bucket_list(plan, bucket_ranges, n_ranges, fn, ranges))
+        return rc;
+    return adam_step(fn, plan, ranges, grads, n_grads, 1, grad_coords, scale, master, exp_avg, exp_avg_sq, param_out,
+                     param_coords, hp, nullptr, main_grad_out, stream);
 }
 
 int sharded_adam_step_clipped(const zdo_plan *plan, const uint16_t *const *grads, int32_t n_grads,
                               int32_t grad_coords, float scale, float *master, float *exp_avg, float *exp_avg_sq,
                               uint16_t *param_out, int32_t param_coords, const zdo_adam *hp,
                               const float *grad_coeff, float *main_grad_out, void *stream) {
+    const char *fn = "sharded_adam_step_clipped";
+    if (int rc = check_plan(plan, fn))
+        return rc;
     if (!grad_coeff)
         return fail(ZDO_EINVAL, "sharded_adam_step_clipped: grad_coeff is NULL");
-    return adam_step("sharded_adam_step_clipped", plan, 0, -1, grads, n_grads, 1, grad_coords, scale, master, exp_avg,
-                     exp_avg_sq, param_out, param_coords, hp, grad_coeff, main_grad_out, stream);
+    return adam_step(fn, plan, all_buckets(plan), grads, n_grads, 1, grad_coords, scale, master, exp_avg, exp_avg_sq,
+                     param_out, param_coords, hp, grad_coeff, main_grad_out, stream);
 }
 
 int sharded_adam_step_instances(const zdo_plan *plan, const uint16_t *const *grads, int32_t n_instances,
@@ -445,8 +560,8 @@ int sharded_adam_step_instances(const zdo_plan *plan, const uint16_t *const *gra
     if (n_instances < 1 || int64_t(n_instances) * plan->dp_size > ZDO_MAX_REPLICAS)
         return fail(ZDO_EINVAL, std::string(fn) + ": n_instances must be >= 1 with n_instances * D <= " +
                                     std::to_string(ZDO_MAX_REPLICAS));
-    return adam_step(fn, plan, 0, -1, grads, n_instances * plan->dp_size, n_instances, grad_coords, scale, master,
-                     exp_avg, exp_avg_sq, param_out, param_coords, hp, nullptr, main_grad_out, stream);
+    return adam_step(fn, plan, all_buckets(plan), grads, n_instances * plan->dp_size, n_instances, grad_coords,
+                     scale, master, exp_avg, exp_avg_sq, param_out, param_coords, hp, nullptr, main_grad_out, stream);
 }
 
 int64_t zdo_plan_norm_workspace_bytes(const zdo_plan *p) {
@@ -497,7 +612,7 @@ static int norm_sq_impl(const char *fn, const zdo_plan *plan, const uint16_t *co
                 return fail(ZDO_EALIAS, std::string(fn) + ": reduced_out overlaps replica " + std::to_string(j) +
                                             " without coinciding with it");
     }
-    a.walk = {plan->d_param_segs, plan->d_param_group, int64_t(plan->param_segs.size()), plan->param_tiles, 0, 0};
+    a.walk = one_run(plan->d_param_segs, plan->d_param_group, int64_t(plan->param_segs.size()), 0, plan->param_tiles);
     a.nrep = n_replicas;
     a.in_local = replica_coords == ZDO_LOCAL;
     a.out_local = out_coords == ZDO_LOCAL;
@@ -571,7 +686,7 @@ int writeback_params(const zdo_plan *plan, const float *master, uint16_t *param_
     if (overlap(span_of(master, plan->shard_numel, 4), span_of(param_out, extent(plan, param_coords), 2)))
         return fail(ZDO_EALIAS, std::string(fn) + ": param_out overlaps master");
     WritebackArgs a{};
-    a.walk = {plan->d_param_segs, plan->d_param_group, int64_t(plan->param_segs.size()), plan->param_tiles, 0, 0};
+    a.walk = one_run(plan->d_param_segs, plan->d_param_group, int64_t(plan->param_segs.size()), 0, plan->param_tiles);
     a.param_local = param_coords == ZDO_LOCAL;
     a.master = master;
     a.param = param_out;

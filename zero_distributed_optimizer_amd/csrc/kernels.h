@@ -12,18 +12,41 @@ struct AdamConst {
     float lr, b1, b2, omb1, omb2, eps, wd, bc1, bc2;
 };
 
+// Disjoint runs of tiles one launch may walk (a list of bucket ranges ready
+// together).
+constexpr int kMaxTileRuns = 16;
+
 // Segments walked by a launch: either a table (nseg segments and their
-// kTileGroup index), of which the launch takes tiles [tile_begin,
-// tile_begin + ntiles), or, when segs is NULL, the single run
-// [0, flat_numel).
+// kTileGroup index) or, when segs is NULL, the single run [0, flat_numel).
+// The launch takes ntiles tiles of that tile space: launch index i in
+// [run_start[r], run_start[r + 1]) is tile run_begin[r] + (i - run_start[r]),
+// for the nruns runs (run_start[0] = 0; one run: tiles [run_begin[0],
+// run_begin[0] + ntiles)).
 struct Walk {
     const Seg *segs;
     const GroupSeg *group;
     int64_t nseg;
     int64_t ntiles;      // tiles in this launch
     int64_t flat_numel;
-    int64_t tile_begin;  // first tile of this launch (a bucket range starts past 0)
+    int32_t nruns;
+    int64_t run_begin[kMaxTileRuns];
+    int64_t run_start[kMaxTileRuns];
 };
+
+// A walk over the one run [first, first + count) of a tile space.
+inline Walk one_run(const Seg *segs, const GroupSeg *group, int64_t nseg, int64_t first, int64_t count,
+                    int64_t flat_numel = 0) {
+    Walk w{};
+    w.segs = segs;
+    w.group = group;
+    w.nseg = nseg;
+    w.ntiles = count;
+    w.flat_numel = flat_numel;
+    w.nruns = 1;
+    w.run_begin[0] = first;
+    w.run_start[0] = 0;
+    return w;
+}
 
 struct ReduceArgs {
     Walk walk;

@@ -27,6 +27,7 @@
 // for bit; the order of operations is the one stated in include/zdo.h.
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <mutex>
 
 #include "kernels.h"
@@ -148,6 +149,24 @@ __device__ __forceinline__ Seg seg_of(const Walk &wk, int64_t tile) {
     return cur;
 }
 
+// The tile at launch index i (wave-uniform). With several runs the run table
+// is read where the launch put it, at the start of the kernel arguments
+// (every walking kernel takes its Walk first), by a scan whose index the
+// compiler cannot hoist out of the tile loop: hoisted, the 32 table entries
+// would stay in scalar registers for the whole kernel.
+static_assert(offsetof(ReduceArgs, walk) == 0 && offsetof(StepArgs, walk) == 0 && offsetof(NormArgs, walk) == 0 &&
+                  offsetof(WritebackArgs, walk) == 0,
+              "tile_at reads the Walk at the start of the kernel arguments");
+__device__ __forceinline__ int64_t tile_at(const Walk &wk, int64_t i) {
+    if (wk.nruns <= 1)
+        return wk.run_begin[0] + i;
+    const ro_ptr<Walk> kw = (ro_ptr<Walk>)(__builtin_amdgcn_kernarg_segment_ptr());
+    int r = 0;
+    while (r + 1 < wk.nruns && i >= kw->run_start[r + 1])
+        ++r;
+    return kw->run_begin[r] + (i - kw->run_start[r]);
+}
+
 // The chunk this thread takes in `tile`; false if it holds no element of the
 // segment.
 __device__ __forceinline__ bool chunk_of(const Walk &wk, int64_t tile, ChunkPos &c) {
@@ -262,8 +281,8 @@ __device__ __forceinline__ void adam(const AdamConst &c, float g, float &p, floa
 
 template <int D>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceArgs a) {
-    for (int64_t tile = a.walk.tile_begin + blockIdx.x; tile < a.walk.tile_begin + a.walk.ntiles;
-         tile += gridDim.x) {
+    for (int64_t i = blockIdx.x; i < a.walk.ntiles; i += gridDim.x) {
+        const int64_t tile = tile_at(a.walk, i);
         ChunkPos c;
         if (!chunk_of(a.walk, tile, c))
             continue;
@@ -310,29 +329,27 @@ struct Quad {
     int lo, hi;      // slots [lo, hi) belong to the segment; none if lo >= hi
 };
 
-// The lane's two quads in `tile`.
-__device__ __forceinline__ void quads_of(const Walk &wk, int64_t tile, Quad q[2]) {
+// The segment walk's view of `tile`: its segment, or the flat run.
+struct SegView {
     int64_t wbeg, lbeg, len, tile0;
+};
+__device__ __forceinline__ SegView seg_view(const Walk &wk, int64_t tile) {
     if (wk.segs) {
         const Seg s = seg_of(wk, tile);
-        wbeg = s.wbeg;
-        lbeg = s.lbeg;
-        len = s.len;
-        tile0 = s.tile0;
-    } else {
-        wbeg = 0;
-        lbeg = 0;
-        len = wk.flat_numel;
-        tile0 = 0;
+        return {s.wbeg, s.lbeg, s.len, s.tile0};
     }
-    const int64_t tw = tile_origin(wbeg) + (tile - tile0) * kTileElems;
-    const int64_t wend = wbeg + len;
+    return {0, 0, wk.flat_numel, 0};
+}
+
+// The lane's two quads of the tile starting at WORLD index tw.
+__device__ __forceinline__ void quads_in(const SegView &s, int64_t tw, Quad q[2]) {
+    const int64_t wend = s.wbeg + s.len;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int64_t w0 = tw + h * (kTileElems / 2) + 4 * int64_t(threadIdx.x);
         q[h].w0 = w0;
-        q[h].k0 = lbeg + (w0 - wbeg);
-        q[h].lo = w0 < wbeg ? (wbeg - w0 < 4 ? int(wbeg - w0) : 4) : 0;
+        q[h].k0 = s.lbeg + (w0 - s.wbeg);
+        q[h].lo = w0 < s.wbeg ? (s.wbeg - w0 < 4 ? int(s.wbeg - w0) : 4) : 0;
         q[h].hi = w0 + 4 > wend ? (wend > w0 ? int(wend - w0) : 0) : 4;
     }
 }
@@ -407,6 +424,99 @@ __device__ __forceinline__ void reduce_quads(const StepArgs &a, const int64_t *g
     }
 }
 
+// Adam and the stores for Q full quads at LOCAL k0[h] / WORLD w0[h], from
+// their state and their reduced gradient (bf16 pairs, red[2h], red[2h + 1]).
+template <int Q, bool kNT>
+__device__ __forceinline__ void finish_quads(const StepArgs &a, const int64_t *k0, const int64_t *w0,
+                                             const f32x4 *pv, const f32x4 *mv, const f32x4 *vv,
+                                             const uint32_t *red, bool clip, float cf) {
+    float g[4 * Q];
+#pragma unroll
+    for (int k = 0; k < 2 * Q; ++k) {
+        g[2 * k] = lo_f32(red[k]);
+        g[2 * k + 1] = hi_f32(red[k]);
+    }
+    if (clip) {
+#pragma unroll
+        for (int e = 0; e < 4 * Q; ++e)
+            g[e] = g[e] * cf;
+    }
+#pragma unroll
+    for (int h = 0; h < Q; ++h) {
+        float p[4], m[4], v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            p[e] = pv[h][e];
+            m[e] = mv[h][e];
+            v[e] = vv[h][e];
+            adam(a.c, g[4 * h + e], p[e], m[e], v[e]);
+        }
+        st_state<kNT>(a.master + k0[h], f32x4{p[0], p[1], p[2], p[3]});
+        st_state<kNT>(a.m + k0[h], f32x4{m[0], m[1], m[2], m[3]});
+        st_state<kNT>(a.v + k0[h], f32x4{v[0], v[1], v[2], v[3]});
+        if (a.main_grad)
+            stf4_out(a.main_grad + k0[h], f32x4{g[4 * h], g[4 * h + 1], g[4 * h + 2], g[4 * h + 3]});
+        if (a.param)
+            st8_out(a.param + (a.param_local ? k0[h] : w0[h]),
+                    u32x2{to_bf16x2(p[0], p[1]), to_bf16x2(p[2], p[3])});
+    }
+}
+
+// A whole tile inside its segment, D contributions by 16-byte loads: lane l
+// reduces the tile's slots [8l, 8l + 8) (one load per contribution, 1 KiB
+// per load instruction), then takes its two quads' reduced values, slots
+// [4l, 4l + 4) and [256 + 4l, 256 + 4l + 4), from lanes l/2 and 32 + l/2
+// through the cross-lane permute; the state stays in the quad layout. Half
+// the load instructions of the quad path, so every load of the tile is in
+// flight at once up to 32 contributions. tw: WORLD index of the tile's first
+// slot; kb: its LOCAL index.
+template <int D, bool kNT>
+__device__ __forceinline__ void step_tile_wide(const StepArgs &a, int64_t tw, int64_t kb, bool clip, float cf) {
+    const int lane = int(threadIdx.x);
+    int64_t k0[2], w0[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        k0[h] = kb + h * (kTileElems / 2) + 4 * lane;
+        w0[h] = tw + h * (kTileElems / 2) + 4 * lane;
+    }
+    f32x4 pv[2], mv[2], vv[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        pv[h] = ld_state<kNT>(a.master + k0[h]);
+        mv[h] = ld_state<kNT>(a.m + k0[h]);
+        vv[h] = ld_state<kNT>(a.v + k0[h]);
+    }
+    const int64_t gi = (a.in_local ? kb : tw) + int64_t(kChunk) * lane;
+    u32x4 r[D];
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+        r[j] = ld_rep(a.rep[j] + gi);
+    float acc[8];
+    first_term(acc, r[0], a.scale);
+#pragma unroll
+    for (int j = 1; j < D; ++j)
+        add_term(acc, r[j], a.scale);
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        w[k] = to_bf16x2(acc[2 * k], acc[2 * k + 1]);
+    // quad 0 of lane l: words 2(l&1), 2(l&1)+1 of lane l/2; quad 1: the same
+    // words of lane 32 + l/2
+    const int src0 = (lane >> 1) << 2, src1 = (32 + (lane >> 1)) << 2;
+    const bool odd = lane & 1;
+    uint32_t red[4];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t a0 = uint32_t(__builtin_amdgcn_ds_bpermute(src0, int(w[k])));
+        const uint32_t a1 = uint32_t(__builtin_amdgcn_ds_bpermute(src0, int(w[k + 2])));
+        const uint32_t b0 = uint32_t(__builtin_amdgcn_ds_bpermute(src1, int(w[k])));
+        const uint32_t b1 = uint32_t(__builtin_amdgcn_ds_bpermute(src1, int(w[k + 2])));
+        red[k] = odd ? a1 : a0;
+        red[2 + k] = odd ? b1 : b0;
+    }
+    finish_quads<2, kNT>(a, k0, w0, pv, mv, vv, red, clip, cf);
+}
+
 // The whole step for Q full quads: reduce, Adam, write-back. The state loads
 // come first, so that they are in flight together with the contributions'
 // loads rather than after the reduction.
@@ -425,38 +535,17 @@ __device__ __forceinline__ void step_quads(const StepArgs &a, const Quad *q, boo
     }
     float acc[4 * Q];
     reduce_quads<D, kInst, Q>(a, gi, acc);
-    float g[4 * Q];
+    uint32_t red[2 * Q];
 #pragma unroll
-    for (int k = 0; k < 2 * Q; ++k) {
-        const uint32_t r = to_bf16x2(acc[2 * k], acc[2 * k + 1]);
-        g[2 * k] = lo_f32(r);
-        g[2 * k + 1] = hi_f32(r);
-    }
-    if (clip) {
-#pragma unroll
-        for (int e = 0; e < 4 * Q; ++e)
-            g[e] = g[e] * cf;
-    }
+    for (int k = 0; k < 2 * Q; ++k)
+        red[k] = to_bf16x2(acc[2 * k], acc[2 * k + 1]);
+    int64_t k0[Q], w0[Q];
 #pragma unroll
     for (int h = 0; h < Q; ++h) {
-        float p[4], m[4], v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            p[e] = pv[h][e];
-            m[e] = mv[h][e];
-            v[e] = vv[h][e];
-            adam(a.c, g[4 * h + e], p[e], m[e], v[e]);
-        }
-        const int64_t k0 = q[h].k0;
-        st_state<kNT>(a.master + k0, f32x4{p[0], p[1], p[2], p[3]});
-        st_state<kNT>(a.m + k0, f32x4{m[0], m[1], m[2], m[3]});
-        st_state<kNT>(a.v + k0, f32x4{v[0], v[1], v[2], v[3]});
-        if (a.main_grad)
-            stf4_out(a.main_grad + k0, f32x4{g[4 * h], g[4 * h + 1], g[4 * h + 2], g[4 * h + 3]});
-        if (a.param)
-            st8_out(a.param + (a.param_local ? k0 : q[h].w0),
-                    u32x2{to_bf16x2(p[0], p[1]), to_bf16x2(p[2], p[3])});
+        k0[h] = q[h].k0;
+        w0[h] = q[h].w0;
     }
+    finish_quads<Q, kNT>(a, k0, w0, pv, mv, vv, red, clip, cf);
 }
 
 // The step for the slots [lo, hi) of a partial quad, one at a time.
@@ -482,6 +571,18 @@ __device__ __forceinline__ void step_slots(const StepArgs &a, const Quad &q, boo
     }
 }
 
+// Whole tiles of a fixed number of contributions, at least ZDO_WIDE_STEP_MIN_D,
+// take step_tile_wide; edge tiles (a quad at a time) and the other forms
+// take the quads. Measured against the quad path in alternating runs on one
+// box: Llama-3-70B shape (32 contributions) 33.87 -> 33.65 ms and 33.68 ->
+// 33.55 ms; fragmentation (16) 48.5 -> 48.7 us; Llama-3-8B (8) 6.84 -> 6.95
+// ms. So only 32 contributions take it.
+#ifndef ZDO_WIDE_STEP_MIN_D
+#define ZDO_WIDE_STEP_MIN_D 32
+#endif
+template <int D, bool kInst>
+constexpr bool kWideStep = !kInst && D >= 1 && D >= ZDO_WIDE_STEP_MIN_D;
+
 // kInst: a.rep holds a.ninst instances of D (or, for D = 0, a.dinst)
 // contributions each; otherwise a.nrep contributions of one instance.
 //
@@ -489,11 +590,12 @@ __device__ __forceinline__ void step_slots(const StepArgs &a, const Quad &q, boo
 // 1 GiB; see launch_step).
 //
 // The occupancy bounds tell the compiler how many waves can share a SIMD,
-// which the launches cap anyway (lds_reserve): with at most 4 (3 for 32
-// contributions, 166 registers), it keeps every load of a tile in flight
-// before the first wait instead of interleaving waits to save registers.
+// which the launches cap anyway (lds_reserve): with at most 4 (2 for 32
+// contributions, whose long launches run 6 waves per compute unit: 1.5 per
+// SIMD), it keeps every load of a tile in flight before the first wait
+// instead of interleaving waits to save registers.
 template <int D, bool kInst, bool kNT>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(D >= 32 && !kInst ? 3 : 1, D < 32 ? 4 : 3)))
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(D >= 32 && !kInst ? 2 : 1, D < 32 ? 4 : 3)))
 void step_kernel(StepArgs a) {
     // Global-norm clipping: the main grad is multiplied by the coefficient; a
     // NaN coefficient (found-inf) leaves everything unchanged.
@@ -502,11 +604,21 @@ void step_kernel(StepArgs a) {
     // body would split the block that issues all of a tile's loads at once.
     const bool clip = a.coeff != nullptr;
     const float cf = clip ? *ro(a.coeff) : 1.0f;
-    const int64_t tend = clip && cf != cf ? a.walk.tile_begin : a.walk.tile_begin + a.walk.ntiles;
-    for (int64_t tile = a.walk.tile_begin + blockIdx.x; tile < tend; tile += gridDim.x) {
+    const int64_t iend = clip && cf != cf ? 0 : a.walk.ntiles;
+    for (int64_t i = blockIdx.x; i < iend; i += gridDim.x) {
+        const int64_t tile = tile_at(a.walk, i);
+        const SegView sv = seg_view(a.walk, tile);
+        const int64_t tw = tile_origin(sv.wbeg) + (tile - sv.tile0) * kTileElems;
+        if constexpr (kWideStep<D, kInst>) {
+            // wave-uniform: the whole tile lies inside the segment
+            if (tw >= sv.wbeg && tw + kTileElems <= sv.wbeg + sv.len) {
+                step_tile_wide<D, kNT>(a, tw, sv.lbeg + (tw - sv.wbeg), clip, cf);
+                continue;
+            }
+        }
         Quad q[2];
-        quads_of(a.walk, tile, q);
-        if (full(q[0]) && full(q[1])) {
+        quads_in(sv, tw, q);
+        if (!kWideStep<D, kInst> && full(q[0]) && full(q[1])) {
             step_quads<D, kInst, 2, kNT>(a, q, clip, cf);
         } else {
 #pragma unroll
@@ -528,8 +640,8 @@ static_assert(kBlock == 64, "the tile reduction below assumes one wave per workg
 
 template <int D>
 __global__ __launch_bounds__(kBlock) void norm_kernel(NormArgs a) {
-    for (int64_t tile = a.walk.tile_begin + blockIdx.x; tile < a.walk.tile_begin + a.walk.ntiles;
-         tile += gridDim.x) {
+    for (int64_t i = blockIdx.x; i < a.walk.ntiles; i += gridDim.x) {
+        const int64_t tile = tile_at(a.walk, i);
         ChunkPos c;
         double s = 0.0;
         if (chunk_of(a.walk, tile, c)) {
@@ -562,7 +674,7 @@ __global__ __launch_bounds__(kBlock) void norm_kernel(NormArgs a) {
         for (int off = 32; off > 0; off >>= 1)
             s = s + __shfl_xor(s, off, 64);
         if (threadIdx.x == 0)
-            a.partial[tile - a.walk.tile_begin] = s;
+            a.partial[i] = s;
     }
 }
 
@@ -627,8 +739,8 @@ __global__ __launch_bounds__(64) void clip_kernel(const double *parts, int32_t n
 // the step.
 template <bool kNT>
 __global__ __launch_bounds__(kBlock) void writeback_kernel(WritebackArgs a) {
-    for (int64_t tile = a.walk.tile_begin + blockIdx.x; tile < a.walk.tile_begin + a.walk.ntiles;
-         tile += gridDim.x) {
+    for (int64_t i = blockIdx.x; i < a.walk.ntiles; i += gridDim.x) {
+        const int64_t tile = tile_at(a.walk, i);
         ChunkPos c;
         if (!chunk_of(a.walk, tile, c))
             continue;

@@ -263,6 +263,10 @@ def main() -> int:
     if not args.no_cpu:
         cpu = cpu_baseline(torch, np, sh, args.cpu_seconds)
 
+    # the ceiling of the step's stream shape: the same traffic with trivial
+    # arithmetic on the same buffers (overwrites their values; last)
+    probe = stream_probe(zdo, torch, sh, stream, min(args.steps, 10), achieved)
+
     del sh
     torch.cuda.synchronize(dev)
     torch.cuda.empty_cache()
@@ -324,6 +328,7 @@ def main() -> int:
                        "flush": "torch sum over a 1 GiB buffer (temporal loads) before every step, outside the "
                                 "kernel's events"},
         "copy_reference_gbps": copy_gbps,
+        "stream_probe": probe,
         "variants": variants,
         "configs": configs,
         "cpu_baseline": cpu,
@@ -334,6 +339,27 @@ def main() -> int:
 
 def sh_coords_world(w) -> bool:
     return w.grad_mode == "world"
+
+
+def stream_probe(zdo, torch, sh, stream, n: int, step_gbps: float) -> dict | None:
+    """zdo_stream_probe on the shard's own buffers: the step's reads and
+    writes (2D + 26 bytes per slot, the same tile and lane layout) with
+    trivial arithmetic, at several occupancy caps; the best is the ceiling
+    of this stream shape on this part."""
+    D = sh.D
+    if D not in (8, 16, 32):
+        return None
+    m = min(sh.plan.shard_numel, sh.n_rep) // 512 * 512
+    out = {"elements": m, "bytes_per_element": 2 * D + 26, "caps": {}}
+    for cap in (4, 5, 6, 8, 10):
+        t, _ = back_to_back(torch, lambda: zdo.stream_probe(sh.reps, sh.state, sh.params, m, cap, stream), stream, n)
+        out["caps"][str(cap)] = rate(m * (2 * D + 26), t)
+    best = max(out["caps"].items(), key=lambda kv: kv[1]["gbps"])
+    out["best"] = {"waves_per_cu": int(best[0]), **best[1]}
+    out["step_vs_best"] = step_gbps / best[1]["gbps"]
+    log(f"stream-shape probe: " + ", ".join(f"{k} waves/CU {v['gbps']:.0f} GB/s" for k, v in out["caps"].items()) +
+        f"; the step runs at {out['step_vs_best']:.1%} of the best")
+    return out
 
 
 # ---- every workload, rank by rank -----------------------------------------------------------------
@@ -373,6 +399,7 @@ def measure_config(zdo, torch, np, W, w, dev, stream, flush_src) -> dict:
            "hbm_frac_min": min(e["frac"] for e in ranks), "hbm_frac_max": max(e["frac"] for e in ranks)}
     if w.name == "frag":
         out["bucket_groups"] = bucket_groups(zdo, torch, big, stream, 100)
+        out["fixed_cost_fit"] = fixed_cost_fit(zdo, torch, np, W, w, dev, stream, flush_src)
         # the force_all_reduce path: the whole reduced buffer (2D + 2 bytes
         # per buffer element)
         Nn = big.plan.buffer_numel
@@ -387,6 +414,32 @@ def measure_config(zdo, torch, np, W, w, dev, stream, flush_src) -> dict:
     del big, reps
     log(f"config {w.name}: " + ", ".join(f"r{e['rank']} {e['frac']:.1%}" for e in ranks) +
         f" ({time.perf_counter() - t0:.1f}s)")
+    return out
+
+
+def fixed_cost_fit(zdo, torch, np, W, w, dev, stream, flush_src) -> dict:
+    """Where a short step's time goes: rank 0's cold-cache step on the
+    parameter list repeated 1, 2 and 4 times (same bucket size and D), fitted
+    as time = fixed + bytes / rate. The fixed part is what one launch costs
+    whatever its size (dispatch, the first loads' latency, the last wave);
+    the rate is the step's streaming rate at this shape."""
+    import dataclasses
+    pts = []
+    for k in (1, 2, 4):
+        wk = dataclasses.replace(w, param_numel=tuple(w.param_numel) * k)
+        sh = Shard(zdo, torch, W, wk, 0, dev)
+        c = cold(torch, np, lambda: sh.step(zdo, stream), stream, flush_src, 40)
+        pts.append((k, sh.alg_bytes, c))
+        del sh
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    x = np.array([p[1] for p in pts], dtype=np.float64)
+    y = np.array([p[2] for p in pts], dtype=np.float64)
+    slope, icpt = np.polyfit(x, y, 1)
+    out = {"repeats": [p[0] for p in pts], "bytes": [p[1] for p in pts], "cold_us": [p[2] * 1e6 for p in pts],
+           "fixed_us": icpt * 1e6, "steady_gbps": 1 / slope / 1e9, "steady_frac": 1 / slope / 1e9 / PEAK_HBM_GBPS}
+    log(f"frag fixed-cost fit: fixed {out['fixed_us']:.1f} us, steady {out['steady_gbps']:.0f} GB/s "
+        f"({out['steady_frac']:.1%})")
     return out
 
 

@@ -363,6 +363,20 @@ int sharded_adam_step_clipped(const zdo_plan *plan, const uint16_t *const *grads
  * counter-calibration reference for the kernels above. */
 int zdo_device_copy(void *dst, const void *src, int64_t bytes, void *stream);
 
+/* The fused step's memory traffic with trivial arithmetic: the ceiling of its
+ * stream shape, measured beside the step (a measurement reference, not part
+ * of the method). Over n elements (a multiple of 512, >= 0): each of the
+ * n_reads bf16 buffers reads[j] is read once (n_reads = 8, 16 or 32), the
+ * three fp32 buffers state0..2 are read and rewritten, and the bf16 buffer
+ * out is written; 2*n_reads + 26 bytes per element, the step's count, every
+ * access non-temporal and in the step's tile and lane layout. The values
+ * written are meaningless (the state gains the exponent bits of the reads'
+ * XOR). waves_per_cu caps the workgroups per compute unit (0: no cap). All
+ * buffers device, 16-byte aligned, n elements, pairwise disjoint
+ * (ZDO_EALIAS); the current device's LDS size sets the cap. */
+int zdo_stream_probe(const uint16_t *const *reads, int32_t n_reads, float *state0, float *state1, float *state2,
+                     uint16_t *out, int64_t n, int32_t waves_per_cu, void *stream);
+
 const char *zdo_last_error(void);
 
 #ifdef __cplusplus

@@ -18,6 +18,7 @@ hipError_t launch_norm(const NormArgs &, double *, int, hipStream_t) { return hi
 hipError_t launch_clip(const double *, int32_t, float, float *, double *, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_gather(const GatherArgs &, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t no_alloc_scratch(void **out) { *out = nullptr; return hipErrorNoDevice; }
+hipError_t launch_probe(const ProbeArgs &, int, int, hipStream_t) { return hipErrorNoDevice; }
 }
 
 int main() {

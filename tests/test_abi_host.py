@@ -27,7 +27,7 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     L = Z.require_library()
     names = header_functions()
-    assert len(names) == 31, names
+    assert len(names) == 32, names
     assert sorted(Z.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n

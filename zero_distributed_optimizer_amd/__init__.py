@@ -70,7 +70,8 @@ EXPORTS = ("build_range_map", "zdo_plan_destroy", "zdo_plan_buffer_numel", "zdo_
            "zdo_plan_norm_workspace_bytes", "grad_norm_sq", "clip_coefficient", "sharded_adam_step_clipped",
            "sharded_adam_step_instances", "all_gather_params", "zdo_device_copy", "zdo_last_error",
            "plan_buckets", "plan_pieces", "plan_buffer_numel", "plan_shard_numel", "plan_destroy",
-           "grad_norm_sq_no_alloc", "reduce_scatter_local_bucket_list", "sharded_adam_step_bucket_list")
+           "grad_norm_sq_no_alloc", "reduce_scatter_local_bucket_list", "sharded_adam_step_bucket_list",
+           "zdo_stream_probe")
 NO_ALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
@@ -125,6 +126,7 @@ def require_library() -> ctypes.CDLL:
                                               vp]
     L.all_gather_params.argtypes = [vp, vp, i32, vp, vp]
     L.zdo_device_copy.argtypes = [vp, vp, i64, vp]
+    L.zdo_stream_probe.argtypes = [vp, i32, vp, vp, vp, vp, i64, i32, vp]
     L.zdo_last_error.argtypes = []
     L.zdo_last_error.restype = ctypes.c_char_p
     for f in ("build_range_map", "zdo_plan_buckets", "zdo_plan_pieces", "plan_buckets", "plan_pieces",
@@ -133,7 +135,7 @@ def require_library() -> ctypes.CDLL:
               "clip_coefficient",
               "sharded_adam_step_clipped", "reduce_scatter_local_buckets", "sharded_adam_step_buckets",
               "sharded_adam_step_instances", "all_gather_params", "zdo_device_copy",
-              "reduce_scatter_local_bucket_list", "sharded_adam_step_bucket_list"):
+              "reduce_scatter_local_bucket_list", "sharded_adam_step_bucket_list", "zdo_stream_probe"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -462,3 +464,14 @@ def device_copy(dst, src, stream=None) -> None:
     if not (dst.is_cuda and src.is_cuda and dst.is_contiguous() and src.is_contiguous()):
         raise ValueError("device_copy: contiguous device tensors required")
     _check(require_library().zdo_device_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream(stream, src.device)))
+
+
+def stream_probe(reads, state, out, n: int, waves_per_cu: int = 0, stream=None) -> None:
+    """The step's stream shape with trivial arithmetic (zdo_stream_probe): the
+    bf16 tensors `reads` are read, the three float32 tensors `state` read and
+    rewritten, `out` (bf16) written, over n elements (a multiple of 512)."""
+    r = _ptr_list(reads, "reads", n)
+    s0, s1, s2 = (_dev_ptr(x, "state", "f32", n) for x in state)
+    o = _dev_ptr(out, "out", "bf16", n)
+    _check(require_library().zdo_stream_probe(r, len(reads), s0, s1, s2, o, n, waves_per_cu,
+                                              _stream(stream, out.device)))

@@ -734,4 +734,47 @@ int zdo_device_copy(void *dst, const void *src, int64_t bytes, void *stream) {
     return launch_result(launch_copy(dst, src, bytes / 16, static_cast<hipStream_t>(stream)), fn);
 }
 
+int zdo_stream_probe(const uint16_t *const *reads, int32_t n_reads, float *state0, float *state1, float *state2,
+                     uint16_t *out, int64_t n, int32_t waves_per_cu, void *stream) {
+    const char *fn = "zdo_stream_probe";
+    if (n_reads != 8 && n_reads != 16 && n_reads != 32)
+        return fail(ZDO_EINVAL, std::string(fn) + ": n_reads must be 8, 16 or 32");
+    if (n < 0 || n % kTileElems != 0)
+        return fail(ZDO_EINVAL, std::string(fn) + ": n must be a non-negative multiple of 512");
+    if (waves_per_cu < 0)
+        return fail(ZDO_EINVAL, std::string(fn) + ": waves_per_cu must be >= 0");
+    if (!reads)
+        return fail(ZDO_EINVAL, std::string(fn) + ": reads is NULL");
+    ProbeArgs a{};
+    Span spans[ZDO_MAX_REPLICAS + 4];
+    for (int32_t j = 0; j < n_reads; ++j) {
+        if (int rc = check_ptr(reads[j], fn, "reads[j]"))
+            return rc;
+        a.rep[j] = reads[j];
+        spans[j] = span_of(reads[j], n, 2);
+    }
+    float *st[3] = {state0, state1, state2};
+    for (int i = 0; i < 3; ++i) {
+        if (int rc = check_ptr(st[i], fn, "state"))
+            return rc;
+        a.state[i] = st[i];
+        spans[n_reads + i] = span_of(st[i], n, 4);
+    }
+    if (int rc = check_ptr(out, fn, "out"))
+        return rc;
+    spans[n_reads + 3] = span_of(out, n, 2);
+    for (int32_t i = 0; i < n_reads + 4; ++i)
+        for (int32_t k = i + 1; k < n_reads + 4; ++k)
+            if (overlap(spans[i], spans[k]))
+                return fail(ZDO_EALIAS, std::string(fn) + ": buffers overlap");
+    int dev = 0, lds = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess)
+        return fail(ZDO_EHIP, std::string(fn) + ": no HIP device");
+    a.nrep = n_reads;
+    a.out = out;
+    a.ntiles = n / kTileElems;
+    return launch_result(launch_probe(a, waves_per_cu, lds, static_cast<hipStream_t>(stream)), fn);
+}
+
 }  // extern "C"

@@ -109,12 +109,25 @@ struct WritebackArgs {
     int64_t state_numel;  // L: the master array's length (selects its cache policy)
 };
 
+// The step's stream shape with trivial arithmetic (zdo_stream_probe): ntiles
+// tiles of 512 elements of nrep bf16 streams (read), three fp32 streams (read
+// and rewritten) and one bf16 stream (written).
+struct ProbeArgs {
+    const uint16_t *rep[ZDO_MAX_REPLICAS];
+    int32_t nrep;
+    float *state[3];
+    uint16_t *out;
+    int64_t ntiles;
+};
+
 // lds_per_cu: LDS bytes per compute unit of the launch device (0 if unknown),
 // used to cap how many workgroups share a compute unit.
 hipError_t launch_reduce(const ReduceArgs &a, int lds_per_cu, hipStream_t stream);
 hipError_t launch_step(const StepArgs &a, int lds_per_cu, hipStream_t stream);
 hipError_t launch_writeback(const WritebackArgs &a, hipStream_t stream);
 hipError_t launch_copy(void *dst, const void *src, int64_t n16, hipStream_t stream);
+// waves_per_cu: occupancy cap (0: none).
+hipError_t launch_probe(const ProbeArgs &a, int waves_per_cu, int lds_per_cu, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs &a, int lds_per_cu, hipStream_t stream);
 // Squared norm: per-tile partials into a.partial, then their fixed-order sum
 // into *norm_sq (0 when a.walk has no tiles).

@@ -801,6 +801,46 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a) {
     }
 }
 
+// The step's stream shape with trivial arithmetic (a measurement reference):
+// per 512-element tile, D bf16 streams read by 16-byte chunks, three fp32
+// streams read and rewritten by two quads per lane, one bf16 stream written by
+// quads, every access non-temporal as in the step on a large shard. The bf16
+// words are XORed and the result's exponent bits added to the fp32 values;
+// every loaded byte feeds a stored one, so no load can be dropped. The
+// occupancy bounds are the step's, so that the compiler likewise issues
+// every load of a tile before the first wait.
+template <int D>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(D >= 32 ? 2 : 1, D < 32 ? 4 : 3)))
+void probe_kernel(ProbeArgs a) {
+    const int lane = int(threadIdx.x);
+    for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+        const int64_t kb = tile * kTileElems;
+        f32x4 s[2][3];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 3; ++i)
+                s[h][i] = ld_state<true>(a.state[i] + kb + h * (kTileElems / 2) + 4 * lane);
+        u32x4 r[D];
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            r[j] = ld_rep(a.rep[j] + kb + int64_t(kChunk) * lane);
+        u32x4 x = r[0];
+#pragma unroll
+        for (int j = 1; j < D; ++j)
+            x ^= r[j];
+        const float f = __uint_as_float((x[0] ^ x[1] ^ x[2] ^ x[3]) & 0x3f000000u);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int i = 0; i < 3; ++i)
+                st_state<true>(a.state[i] + kb + h * (kTileElems / 2) + 4 * lane, s[h][i] + f);
+            st8_out(a.out + kb + h * (kTileElems / 2) + 4 * lane,
+                    u32x2{__float_as_uint(s[h][0][0]) ^ x[2 * h], __float_as_uint(s[h][1][1]) ^ x[2 * h + 1]});
+        }
+    }
+}
+
 __global__ __launch_bounds__(kBlock) void copy_kernel(u32x4 *dst, const u32x4 *src, int64_t n16) {
     for (int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x; i < n16; i += int64_t(gridDim.x) * kBlock)
         __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
@@ -1031,6 +1071,20 @@ hipError_t launch_gather(const GatherArgs &a, int lds_per_cu, hipStream_t stream
         return hipSuccess;
     hipLaunchKernelGGL(gather_kernel, dim3(grid_for(a.ntiles)), dim3(kBlock), lds_for_waves(lds_per_cu, kGatherWaves),
                        stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe(const ProbeArgs &a, int waves_per_cu, int lds_per_cu, hipStream_t stream) {
+    if (a.ntiles <= 0)
+        return hipSuccess;
+    const dim3 grid(grid_for(a.ntiles)), block(kBlock);
+    const unsigned lds = lds_for_waves(lds_per_cu, waves_per_cu);
+    switch (a.nrep) {
+    case 8: hipLaunchKernelGGL(probe_kernel<8>, grid, block, lds, stream, a); break;
+    case 16: hipLaunchKernelGGL(probe_kernel<16>, grid, block, lds, stream, a); break;
+    case 32: hipLaunchKernelGGL(probe_kernel<32>, grid, block, lds, stream, a); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -135,3 +135,54 @@ def test_graph_zero1_loop_and_instances(gpu):
         assert torch.equal(graphed["inst_params"], eager["inst_params"]), f"replay {replay} instances"
     del g
     free()
+
+
+def _groups(gpu, plan, reps, w, st, par, red, ns, groups, hpk):
+    """Bucket-list launches (their run table read from the kernel
+    arguments), and the squared norm on the library's static scratch."""
+    for g in groups:
+        gpu.sharded_adam_step(plan, reps, gpu.WORLD, w.scale, *st, par, gpu.WORLD, buckets=g, **hpk)
+        gpu.reduce_scatter_local(plan, reps, gpu.WORLD, w.scale, red, gpu.WORLD, buckets=g)
+    gpu.grad_norm_sq_no_alloc(plan, reps, gpu.WORLD, w.scale, ns)
+
+
+def test_graph_bucket_lists_and_no_alloc_norm(gpu):
+    """Launches over lists of scattered bucket ranges and the allocation-free
+    squared norm, captured once and replayed four times with eager work in
+    between: every replay equals the eager calls."""
+    w = W.get("frag")
+    D = w.dp_size
+    N = OL.build_layout(w.param_numel, w.bucket_numel, D).buffer_numel
+    plan = gpu.build_range_map(w.param_numel, w.bucket_numel, D, 3)
+    nb = plan.buckets().size
+    groups = [[(b, b + 1) for b in range(k, nb, 3)] for k in (2, 0, 1)]
+    reps = _gen_world(w, N)
+    hpk = hp_kwargs(w.hp, 4)
+
+    def fresh():
+        return dict(st=_gen_state(w, plan.shard_numel), par=torch.full((N,), SENTINEL, dtype=torch.int16, device=DEV),
+                    red=torch.full((N,), SENTINEL, dtype=torch.int16, device=DEV),
+                    ns=torch.zeros(1, dtype=torch.float64, device=DEV))
+
+    eager, graphed = fresh(), fresh()
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            _groups(gpu, plan, reps, w, graphed["st"], graphed["par"], graphed["red"], graphed["ns"], groups, hpk)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    for replay in range(4):
+        g.replay()
+        _groups(gpu, plan, reps, w, eager["st"], eager["par"], eager["red"], eager["ns"], groups, hpk)
+        torch.cuda.synchronize()
+        scratch = torch.randn(1 << 20, device=DEV)
+        scratch.mul_(2.0)
+        for x, y in zip(graphed["st"], eager["st"]):
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32)), f"replay {replay}"
+        assert torch.equal(graphed["par"], eager["par"]), f"replay {replay} params"
+        assert torch.equal(graphed["red"], eager["red"]), f"replay {replay} reduce-scatter"
+        assert torch.equal(graphed["ns"], eager["ns"]), f"replay {replay} squared norm"
+    del g
+    free()

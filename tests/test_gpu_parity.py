@@ -824,14 +824,18 @@ def test_zero1_loop_step_then_all_gather(gpu, name):
     free()
 
 
-@pytest.mark.parametrize("off_bytes", [16, 48])
-def test_buffers_off_the_cache_line(gpu, off_bytes):
+@pytest.mark.parametrize("off_bytes,D", [(16, 4), (48, 4), (16, 32), (48, 32)])
+def test_buffers_off_the_cache_line(gpu, off_bytes, D):
     """The ABI asks for 16-byte alignment only; the kernels' tiles are laid
     out for 128-byte lines. Every buffer here starts off_bytes past a line:
-    reduce-scatter, the fused step, the clipped path and the all-gather stay
-    bit-exact against the oracle."""
-    rng = np.random.default_rng(off_bytes)
-    sizes, bucket, D = [5000, 13, 20000, 1, 4097, 777], 9000, 4
+    reduce-scatter, the fused step (at D = 32 whole tiles take the 16-byte
+    reduction), the clipped path and the all-gather stay bit-exact against
+    the oracle."""
+    rng = np.random.default_rng(off_bytes + D)
+    if D == 4:
+        sizes, bucket = [5000, 13, 20000, 1, 4097, 777], 9000
+    else:
+        sizes, bucket = [500000, 13, 200000, 1, 40097, 777], 300000
     lay = OL.build_layout(sizes, bucket, D)
     N = lay.buffer_numel
 

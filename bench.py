@@ -151,11 +151,15 @@ def back_to_back(torch, fn, stream, n: int, warmup: int = 3) -> tuple:
     return a.elapsed_time(b) / 1e3 / n, (time.perf_counter() - w0) / n
 
 
+COLD_SPREAD = {}
+
+
 def cold(torch, np, fn, stream, flush_src, n: int) -> float:
     """Seconds per call (mean over n) of calls each after 1 GiB of ordinary
     (temporal) reads, which evict the 256 MB Infinity Cache and the L2s as a
     training step's forward and backward passes would; the event pair
-    brackets the call only."""
+    brackets the call only. The median, p10 and p90 of the n calls (us) are
+    left in COLD_SPREAD."""
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
     for a, b in ev:
         flush_src.sum()
@@ -163,12 +167,19 @@ def cold(torch, np, fn, stream, flush_src, n: int) -> float:
         fn()
         b.record(stream)
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    ms = [a.elapsed_time(b) for a, b in ev]
+    COLD_SPREAD.clear()
+    COLD_SPREAD.update(median_us=float(np.median(ms)) * 1e3, p10_us=float(np.percentile(ms, 10)) * 1e3,
+                       p90_us=float(np.percentile(ms, 90)) * 1e3, calls=n)
+    return float(np.mean(ms)) / 1e3
 
 
-def rate(alg_bytes: float, seconds: float) -> dict:
+def rate(alg_bytes: float, seconds: float, spread: dict | None = None) -> dict:
     gbps = alg_bytes / seconds / 1e9
-    return {"us": seconds * 1e6, "gbps": gbps, "frac": gbps / PEAK_HBM_GBPS}
+    out = {"us": seconds * 1e6, "gbps": gbps, "frac": gbps / PEAK_HBM_GBPS}
+    if spread:
+        out["spread"] = dict(spread)
+    return out
 
 
 # ---- main ------------------------------------------------------------------------------------
@@ -252,7 +263,7 @@ def main() -> int:
     log(f"copy reference: {copy_gbps:.0f} GB/s")
 
     cold_s = cold(torch, np, lambda: sh.step(zdo, stream), stream, flush_src, min(args.steps, 20))
-    cold_r = rate(sh.alg_bytes, cold_s)
+    cold_r = rate(sh.alg_bytes, cold_s, COLD_SPREAD)
     log(f"cold caches: kernel avg {cold_s * 1e6:.1f} us, {cold_r['gbps']:.0f} GB/s algorithmic")
 
     variants = None
@@ -324,10 +335,11 @@ def main() -> int:
                    "source_sha256_16": kernel_source_hash(),
                    "state_in_infinity_cache": in_cache},
         "cold_cache": {"kernel_avg_us": cold_s * 1e6, "achieved_gbps": cold_r["gbps"], "frac": cold_r["frac"],
-                       "elements_per_s": E / cold_s,
+                       "elements_per_s": E / cold_s, "spread": cold_r["spread"],
                        "flush": "torch sum over a 1 GiB buffer (temporal loads) before every step, outside the "
                                 "kernel's events"},
         "copy_reference_gbps": copy_gbps,
+        "frac_of_copy_reference": achieved / copy_gbps,
         "stream_probe": probe,
         "variants": variants,
         "configs": configs,
@@ -384,7 +396,7 @@ def measure_config(zdo, torch, np, W, w, dev, stream, flush_src) -> dict:
                  "back_to_back": rate(sh.alg_bytes, b2b)}
         if small:
             c = cold(torch, np, lambda: sh.step(zdo, stream), stream, flush_src, 50)
-            entry["cold_cache"] = rate(sh.alg_bytes, c)
+            entry["cold_cache"] = rate(sh.alg_bytes, c, COLD_SPREAD)
             hbm = entry["cold_cache"]
             entry["hbm_figure"] = "cold_cache"
         else:
@@ -409,7 +421,7 @@ def measure_config(zdo, torch, np, W, w, dev, stream, flush_src) -> dict:
         c = cold(torch, np, fn, stream, flush_src, 20)
         out["force_all_reduce"] = {"elements": Nn, "bytes_per_element": 2 * w.dp_size + 2,
                                    "back_to_back": rate(Nn * (2 * w.dp_size + 2), b2b),
-                                   "cold_cache": rate(Nn * (2 * w.dp_size + 2), c)}
+                                   "cold_cache": rate(Nn * (2 * w.dp_size + 2), c, COLD_SPREAD)}
         del full
     del big, reps
     log(f"config {w.name}: " + ", ".join(f"r{e['rank']} {e['frac']:.1%}" for e in ranks) +

@@ -1,7 +1,8 @@
 // Device kernels for gfx950 (CDNA4): the fused sharded Adam step, the
 // reduce-scatter / all-reduce of the D contributions, the squared gradient
 // norm and clipping coefficient, the parameter write-back, the parameter
-// all-gather and a plain copy.
+// all-gather, and two measurement references (a plain copy and the step's
+// stream shape with trivial arithmetic).
 //
 // Every kernel is a stream: the step moves (2D + 26) bytes per element
 // against a few dozen VALU operations, so it is bound by HBM bandwidth, not
@@ -13,8 +14,11 @@
 // 1 KiB of every bf16 stream and 2 KiB of every fp32 stream, contiguously.
 // In the reduce, norm and write-back kernels lane l takes the 8-element
 // chunk [8l, 8l + 8) of the tile (one 16-byte load per bf16 stream); the
-// step takes two quads per lane and the all-gather 2048-element tiles (see
-// there). Chunks or quads cut by a segment's ends take a per-element path.
+// step takes two quads per lane (at 32 contributions it reduces whole tiles
+// by 8-element chunks and moves the results to the quads across lanes) and
+// the all-gather 2048-element tiles (see there). Chunks or quads cut by a
+// segment's ends take a per-element path. A launch walks one run of tiles,
+// or up to 16 runs (a list of bucket ranges) through tile_at.
 //
 // HBM serves this mix of many read streams and some write streams best when
 // few requestors share it: one-wave workgroups, a number per compute unit

@@ -993,3 +993,33 @@ def test_bucket_lists(gpu, name):
     assert (host_u16(par) == SENTINEL).all()
     del reps_d
     free()
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_d32_whole_tiles_and_edges(gpu, seed):
+    """32 contributions: whole tiles take the 16-byte reduction with the
+    cross-lane move to the quads; tiles at a segment's ends take the quads
+    one at a time, partial quads slot by slot. Layouts whose buckets start
+    and end off every 64-element line, so that both paths and the seams
+    between them run in every rank's segments; all ranks are compared with
+    the oracle, WORLD and LOCAL coordinates."""
+    pr = random.Random(4400 + seed)
+    rng = np.random.default_rng(4400 + seed)
+    D = 32
+    sizes = []
+    while sum(sizes) < 32 * 9000:
+        sizes.append(pr.choice([pr.randint(1, 70), pr.randint(500, 3000), pr.randint(20000, 90000)]))
+    bucket = pr.randint(sum(sizes) // 6, sum(sizes) // 3)
+    lay = OL.build_layout(sizes, bucket, D)
+    N = lay.buffer_numel
+    assert all(any(OL.rank_range(b, D, r).start % 64 for b in lay.buckets) for r in (1, D - 1))
+    reps_h = [bf16_host(rng, N, pr.choice([1e-3, 1.0])) for _ in range(D)]
+    hp = W.get("tiny").hp
+    for r in sorted({0, 1, pr.randrange(D), D - 1}):
+        Ln = OL.shard_numel(lay, r)
+        state = [(rng.standard_normal(Ln) * 0.02).astype(np.float32),
+                 (rng.standard_normal(Ln) * 1e-3).astype(np.float32),
+                 ((rng.standard_normal(Ln) * 1e-3) ** 2).astype(np.float32)]
+        c = gpu.WORLD if r % 2 else gpu.LOCAL
+        run_rank_step(gpu, sizes, bucket, D, r, reps_h, state, 1.0 / D, hp, 5, c, gpu.LOCAL if r % 2 else gpu.WORLD)
+    free()

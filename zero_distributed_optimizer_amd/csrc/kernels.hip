@@ -18,7 +18,8 @@
 // by 8-element chunks and moves the results to the quads across lanes) and
 // the all-gather 2048-element tiles (see there). Chunks or quads cut by a
 // segment's ends take a per-element path. A launch walks one run of tiles,
-// or up to 16 runs (a list of bucket ranges) through tile_at.
+// or up to 16 runs (a list of bucket ranges) through tile_at; a short launch
+// hands each XCD 8 consecutive tiles at a time (launch_index).
 //
 // HBM serves this mix of many read streams and some write streams best when
 // few requestors share it: one-wave workgroups, a number per compute unit
@@ -151,6 +152,30 @@ __device__ __forceinline__ Seg seg_of(const Walk &wk, int64_t tile) {
         ++si;
     }
     return cur;
+}
+
+// Launches of fewer tiles than this are short: one workgroup per tile (the
+// grid cap is far above it), a few rounds of waves over the chip.
+constexpr int64_t kShortLaunchTiles = int64_t(1) << 17;
+
+// The launch index that launch slot i (a workgroup's blockIdx.x, plus the
+// grid stride when the grid is capped) takes. The dispatcher hands
+// workgroups to the 8 XCDs in turn, workgroup i to XCD i mod 8. In a short
+// launch each XCD takes 8 consecutive launch indices out of every 64 instead
+// of every 8th: within each block of 64 slots the 8 x 8 order is transposed,
+// a bijection; the slots after the last whole block keep their index. Short
+// launches ran faster so (fragmentation workload, rank 0: 52.2 -> 51.3 us
+// with cold caches, 45.5 -> 44.5 back to back; GPT-2 shape 102.9 -> 101.4
+// us cold), long ones slower (Llama-3-70B shape 33.4 -> 34.6 ms, Llama-3-8B
+// 6.87 -> 7.12 ms), so long launches keep the dispatch order. Kernels that
+// store per-index results (the squared norm's tile partials) store them at
+// the launch index, so their order does not change.
+constexpr int64_t kXcds = 8, kXcdRun = 8, kXcdBlock = kXcds * kXcdRun;
+__device__ __forceinline__ int64_t launch_index(const Walk &wk, int64_t i) {
+    if (wk.ntiles >= kShortLaunchTiles || i >= wk.ntiles / kXcdBlock * kXcdBlock)
+        return i;
+    const int64_t r = i % kXcdBlock;
+    return i - r + (r % kXcds) * kXcdRun + r / kXcds;
 }
 
 // The tile at launch index i (wave-uniform). With several runs the run table
@@ -286,7 +311,8 @@ __device__ __forceinline__ void adam(const AdamConst &c, float g, float &p, floa
 template <int D>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceArgs a) {
     for (int64_t i = blockIdx.x; i < a.walk.ntiles; i += gridDim.x) {
-        const int64_t tile = tile_at(a.walk, i);
+        const int64_t j = launch_index(a.walk, i);
+        const int64_t tile = tile_at(a.walk, j);
         ChunkPos c;
         if (!chunk_of(a.walk, tile, c))
             continue;
@@ -610,7 +636,8 @@ void step_kernel(StepArgs a) {
     const float cf = clip ? *ro(a.coeff) : 1.0f;
     const int64_t iend = clip && cf != cf ? 0 : a.walk.ntiles;
     for (int64_t i = blockIdx.x; i < iend; i += gridDim.x) {
-        const int64_t tile = tile_at(a.walk, i);
+        const int64_t j = launch_index(a.walk, i);
+        const int64_t tile = tile_at(a.walk, j);
         const SegView sv = seg_view(a.walk, tile);
         const int64_t tw = tile_origin(sv.wbeg) + (tile - sv.tile0) * kTileElems;
         if constexpr (kWideStep<D, kInst>) {
@@ -645,7 +672,8 @@ static_assert(kBlock == 64, "the tile reduction below assumes one wave per workg
 template <int D>
 __global__ __launch_bounds__(kBlock) void norm_kernel(NormArgs a) {
     for (int64_t i = blockIdx.x; i < a.walk.ntiles; i += gridDim.x) {
-        const int64_t tile = tile_at(a.walk, i);
+        const int64_t j = launch_index(a.walk, i);
+        const int64_t tile = tile_at(a.walk, j);
         ChunkPos c;
         double s = 0.0;
         if (chunk_of(a.walk, tile, c)) {
@@ -678,7 +706,7 @@ __global__ __launch_bounds__(kBlock) void norm_kernel(NormArgs a) {
         for (int off = 32; off > 0; off >>= 1)
             s = s + __shfl_xor(s, off, 64);
         if (threadIdx.x == 0)
-            a.partial[i] = s;
+            a.partial[j] = s;
     }
 }
 
@@ -744,7 +772,8 @@ __global__ __launch_bounds__(64) void clip_kernel(const double *parts, int32_t n
 template <bool kNT>
 __global__ __launch_bounds__(kBlock) void writeback_kernel(WritebackArgs a) {
     for (int64_t i = blockIdx.x; i < a.walk.ntiles; i += gridDim.x) {
-        const int64_t tile = tile_at(a.walk, i);
+        const int64_t j = launch_index(a.walk, i);
+        const int64_t tile = tile_at(a.walk, j);
         ChunkPos c;
         if (!chunk_of(a.walk, tile, c))
             continue;
@@ -891,7 +920,6 @@ unsigned grid_for(int64_t ntiles) {
 // 344-345 us at 10, 335-338 at 8, 358-362 at 7) and with 7 at 16
 // (fragmentation workload: 414-415 us at 10, 413-414 at 8, 394-395 at 7).
 constexpr int flat_waves(int nrep) { return nrep >= 16 ? 7 : 8; }
-constexpr int64_t kShortLaunchTiles = int64_t(1) << 17;
 
 // LDS per workgroup that lets at most `waves` waves share a compute unit.
 unsigned lds_for_waves(int lds_per_cu, int waves) {

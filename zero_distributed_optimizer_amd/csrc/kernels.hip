@@ -164,10 +164,10 @@ constexpr int64_t kShortLaunchTiles = int64_t(1) << 17;
 // launch each XCD takes 8 consecutive launch indices out of every 64 instead
 // of every 8th: within each block of 64 slots the 8 x 8 order is transposed,
 // a bijection; the slots after the last whole block keep their index. Short
-// launches ran faster so (fragmentation workload, rank 0: 52.2 -> 51.3 us
-// with cold caches, 45.5 -> 44.5 back to back; GPT-2 shape 102.9 -> 101.4
-// us cold), long ones slower (Llama-3-70B shape 33.4 -> 34.6 ms, Llama-3-8B
-// 6.87 -> 7.12 ms), so long launches keep the dispatch order. Kernels that
+// launches ran faster so (fragmentation workload, rank 0: step 48.2 -> 45.0
+// us back to back, 53.6 -> 51.0 us with cold caches; GPT-2 shape within 1%),
+// long ones slower (Llama-3-70B shape 33.4 -> 34.6 ms, Llama-3-8B 6.87 ->
+// 7.12 ms), so long launches keep the dispatch order. Kernels that
 // store per-index results (the squared norm's tile partials) store them at
 // the launch index, so their order does not change.
 constexpr int64_t kXcds = 8, kXcdRun = 8, kXcdBlock = kXcds * kXcdRun;

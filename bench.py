@@ -401,7 +401,7 @@ def measure_config(zdo, torch, np, W, w, dev, stream, flush_src) -> dict:
         entry = {"rank": r, "owned_elements": sh.E, "bytes_per_element": sh.bytes_per_elem,
                  "back_to_back": rate(sh.alg_bytes, b2b)}
         if small:
-            c = cold(torch, np, lambda: sh.step(zdo, stream), stream, flush_src, 50)
+            c = cold(torch, np, lambda: sh.step(zdo, stream), stream, flush_src, 200)
             entry["cold_cache"] = rate(sh.alg_bytes, c, COLD_SPREAD)
             hbm = entry["cold_cache"]
             entry["hbm_figure"] = "cold_cache"

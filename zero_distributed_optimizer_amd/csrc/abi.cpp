@@ -161,11 +161,12 @@ int check_bucket_list(const zdo_plan *plan, const int32_t *pairs, int32_t n, con
     if (n < 0 || (n > 0 && !pairs))
         return fail(ZDO_EINVAL, std::string(fn) + ": need n_ranges >= 0 and a range array");
     out.clear();
-    for (int32_t i = 0; i < n; ++i) {
-        if (int rc = check_buckets(plan, pairs[2 * i], pairs[2 * i + 1], fn))
+    for (int64_t i = 0; i < n; ++i) {
+        const int32_t b0 = pairs[2 * i], b1 = pairs[2 * i + 1];
+        if (int rc = check_buckets(plan, b0, b1, fn))
             return rc;
-        if (pairs[2 * i] < pairs[2 * i + 1])
-            out.emplace_back(pairs[2 * i], pairs[2 * i + 1]);
+        if (b0 < b1)
+            out.emplace_back(b0, b1);
     }
     std::sort(out.begin(), out.end());
     for (size_t i = 1; i < out.size(); ++i)

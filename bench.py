@@ -292,7 +292,8 @@ def main() -> int:
         for name in ("tiny", "gpt2_small", "llama3_8b", "llama3_70b", "frag"):
             if name == w.name:
                 continue
-            configs[name] = measure_config(zdo, torch, np, W, W.get(name), dev, stream, flush_src)
+            configs[name] = measure_config(zdo, torch, np, W, W.get(name), dev, stream, flush_src,
+                                           variants=not args.no_variants)
             torch.cuda.synchronize(dev)
             torch.cuda.empty_cache()
 
@@ -382,11 +383,14 @@ def stream_probe(zdo, torch, sh, stream, n: int, step_gbps: float) -> dict | Non
 
 # ---- every workload, rank by rank -----------------------------------------------------------------
 
-def measure_config(zdo, torch, np, W, w, dev, stream, flush_src) -> dict:
+def measure_config(zdo, torch, np, W, w, dev, stream, flush_src, variants: bool = True) -> dict:
     """Every rank the workload times: the step back to back and with cold
     caches. HBM figure: cold caches where the rank's fp32 state fits in 1 GiB
     (back-to-back steps there read part of it from the Infinity Cache),
-    back to back otherwise (the state streams from HBM either way)."""
+    back to back otherwise (the state streams from HBM either way). On the
+    Llama-3-8B shape also the library's other calls (measure_variants): two
+    instances and the all-gather fit beside it, which they do not beside the
+    Llama-3-70B shard."""
     t0 = time.perf_counter()
     ranks = []
     reps = None
@@ -429,6 +433,8 @@ def measure_config(zdo, torch, np, W, w, dev, stream, flush_src) -> dict:
                                    "back_to_back": rate(Nn * (2 * w.dp_size + 2), b2b),
                                    "cold_cache": rate(Nn * (2 * w.dp_size + 2), c, COLD_SPREAD)}
         del full
+    if w.name == "llama3_8b" and variants:
+        out["variants"] = measure_variants(zdo, torch, np, big.plan, w, big.reps, big.coords, stream, 10)
     del big, reps
     log(f"config {w.name}: " + ", ".join(f"r{e['rank']} {e['frac']:.1%}" for e in ranks) +
         f" ({time.perf_counter() - t0:.1f}s)")

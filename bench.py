@@ -206,7 +206,7 @@ def main() -> int:
                     help="extra bytes (a multiple of 16) placed between consecutive input buffers")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only: the D ranks' contributions are D "
+        print(json.dumps({"error": "bench.py measures one GPU only: the D ranks' contributions are D "
                           "replica buffers in one GPU's HBM; run with --gpus 1"}), flush=True)
         return 2
     if args.stagger % 16:

@@ -912,25 +912,35 @@ def test_buffers_off_the_cache_line(gpu, off_bytes, D):
     free()
 
 
-@pytest.mark.parametrize("name", ["frag", "many"])
+@pytest.mark.parametrize("name", ["frag", "many", "d32"])
 def test_bucket_lists(gpu, name):
     """Page 1, §4.2: several bucket ranges ready together go in one launch
     (sharded_adam_step_bucket_list, reduce_scatter_local_bucket_list).
     Groups of non-adjacent buckets, launched group by group in shuffled
     order, equal the full call and the oracle bit for bit; a list with more
     than 16 separate runs (two launches) too; overlapping or out-of-range
-    lists are EINVAL and an empty list changes nothing."""
+    lists are EINVAL and an empty list changes nothing. "d32": 32
+    contributions, so that whole tiles take the 16-byte reduction inside
+    launches of several runs."""
     if name == "frag":
         w = W.get("frag")
         sizes, bucket, D, r = w.param_numel, w.bucket_numel, w.dp_size, 5
         lay = OL.build_layout(sizes, bucket, D)
         reps_d = _gen_world(w, lay.buffer_numel)
         reps_h = [host_u16(x) for x in reps_d]
-    else:
+    elif name == "many":
         rng = np.random.default_rng(78)
         pr = random.Random(78)
         sizes = [pr.choice([1, 7, 300, 2048, 5000]) for _ in range(120)]
         bucket, D, r = 2000, 3, 2
+        lay = OL.build_layout(sizes, bucket, D)
+        reps_h = [bf16_host(rng, lay.buffer_numel) for _ in range(D)]
+        reps_d = [to_dev(x) for x in reps_h]
+    else:
+        rng = np.random.default_rng(79)
+        pr = random.Random(79)
+        sizes = [pr.choice([1, 70, 3000, 9000, 40000]) for _ in range(260)]
+        bucket, D, r = 60000, 32, 17
         lay = OL.build_layout(sizes, bucket, D)
         reps_h = [bf16_host(rng, lay.buffer_numel) for _ in range(D)]
         reps_d = [to_dev(x) for x in reps_h]
@@ -971,7 +981,7 @@ def test_bucket_lists(gpu, name):
     # there are more than 32 buckets
     evens = [(b, b + 1) for b in range(0, nb, 2)]
     odds = [(b, b + 1) for b in range(1, nb, 2)][::-1]
-    if name == "many":
+    if name != "frag":
         assert len(evens) > 16
     check([evens, odds], "alternate buckets")
     # one list covering everything (touching ranges merge into one run)

@@ -412,3 +412,34 @@ def test_rank_norm_sq_exact_and_summing_to_the_global_norm(seed):
     red = N.widen(S.all_reduce(grads, scale)).astype(np.float64)
     assert global_sq == float(np.sum(red[is_param] ** 2))
     assert global_sq == float(np.sum(sq[is_param]))
+
+
+@pytest.mark.parametrize("name", ["tiny", "gpt2_small", "llama3_8b", "llama3_70b", "frag"])
+def test_rank_state_is_the_zero1_share(name):
+    """Page "Megatron-LM 与 ZeRO" (its per-stage memory accounting): ZeRO
+    stage 1 keeps the bf16 weights and gradients whole on every rank (2 + 2
+    bytes per element) and gives each rank a 1/D share of the 12 bytes of
+    fp32 Adam state; stages 2 and 3 shard the gradients, then the weights
+    too, so a rank's bytes fall from stage 0 to stage 3. The ranks' owned
+    elements count every parameter element once, and each rank's fp32 shard
+    (its range of every padded bucket plus alignment gaps of fewer than 64
+    slots) comes within 12 x 64 bytes per bucket of the stage-1 share
+    12 N / D of the padded buffer."""
+    w = W.get(name)
+    lay = L.build_layout(w.param_numel, w.bucket_numel, w.dp_size)
+    D, N, nb = w.dp_size, lay.buffer_numel, len(lay.buckets)
+    assert sum(L.owned_numel(lay, r) for r in range(D)) == sum(w.param_numel)
+
+    def rank_bytes(stage):
+        per_element = {"weights": 2, "grads": 2, "adam": 12}
+        sharded = {0: (), 1: ("adam",), 2: ("grads", "adam"), 3: ("weights", "grads", "adam")}[stage]
+        return N * sum(b / D if part in sharded else b for part, b in per_element.items())
+
+    stages = [rank_bytes(s) for s in range(4)]
+    if D > 1:
+        assert stages[3] < stages[2] < stages[1] < stages[0]
+    for r in range(D):
+        shard = L.shard_numel(lay, r)
+        assert N // D <= shard < N // D + 64 * nb
+        ours = 2 * N + 2 * N + 12 * shard     # whole bf16 parameter and grad buffers, the fp32 shard
+        assert stages[1] <= ours < stages[1] + 12 * 64 * nb

@@ -364,7 +364,10 @@ def stream_probe(zdo, torch, sh, stream, n: int, step_gbps: float) -> dict | Non
     """zdo_stream_probe on the shard's own buffers: the step's reads and
     writes (2D + 26 bytes per slot, the same tile and lane layout) with
     trivial arithmetic, at several occupancy caps; the best is the ceiling
-    of this stream shape on this part."""
+    of this stream shape on this part. At the best cap, the same loads with
+    only the parameter stream stored (2D + 14 bytes per slot) and with no
+    stores (2D + 12) take the shape apart: what the loads alone reach, and
+    what the state's stores cost."""
     D = sh.D
     if D not in (8, 16, 32):
         return None
@@ -376,8 +379,18 @@ def stream_probe(zdo, torch, sh, stream, n: int, step_gbps: float) -> dict | Non
     best = max(out["caps"].items(), key=lambda kv: kv[1]["gbps"])
     out["best"] = {"waves_per_cu": int(best[0]), **best[1]}
     out["step_vs_best"] = step_gbps / best[1]["gbps"]
+    cap = int(best[0])
+    parts = {}
+    for name, stores, bpe in (("param_stores_only", zdo.PROBE_STORE_OUT, 2 * D + 14),
+                              ("loads_only", zdo.PROBE_STORE_NONE, 2 * D + 12)):
+        t, _ = back_to_back(torch, lambda: zdo.stream_probe(sh.reps, sh.state, sh.params, m, cap, stream,
+                                                            stores=stores), stream, n)
+        parts[name] = {"bytes_per_element": bpe, **rate(m * bpe, t)}
+    out["parts_at_best_cap"] = parts
     log(f"stream-shape probe: " + ", ".join(f"{k} waves/CU {v['gbps']:.0f} GB/s" for k, v in out["caps"].items()) +
-        f"; the step runs at {out['step_vs_best']:.1%} of the best")
+        f"; the step runs at {out['step_vs_best']:.1%} of the best; at {cap} waves/CU the loads with the "
+        f"parameter stores only reach {parts['param_stores_only']['frac']:.1%} of 8 TB/s, the loads alone "
+        f"{parts['loads_only']['frac']:.1%}")
     return out
 
 

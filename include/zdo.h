@@ -363,19 +363,35 @@ int sharded_adam_step_clipped(const zdo_plan *plan, const uint16_t *const *grads
  * counter-calibration reference for the kernels above. */
 int zdo_device_copy(void *dst, const void *src, int64_t bytes, void *stream);
 
+/* Which stores zdo_stream_probe makes. */
+#define ZDO_PROBE_STORE_ALL 0   /* the step's: state rewritten, out written */
+#define ZDO_PROBE_STORE_OUT 1   /* out written, the state only read */
+#define ZDO_PROBE_STORE_NONE 2  /* loads only: one 4-byte word per tile into out */
+
 /* The fused step's memory traffic with trivial arithmetic: the ceiling of its
  * stream shape, measured beside the step (a measurement reference, not part
- * of the method). Over n elements (a multiple of 512, >= 0): each of the
- * n_reads bf16 buffers reads[j] is read once (n_reads = 8, 16 or 32), the
- * three fp32 buffers state0..2 are read and rewritten, and the bf16 buffer
- * out is written; 2*n_reads + 26 bytes per element, the step's count, every
- * access non-temporal and in the step's tile and lane layout. The values
- * written are meaningless (the state gains the exponent bits of the reads'
- * XOR). waves_per_cu caps the workgroups per compute unit (0: no cap). All
- * buffers device, 16-byte aligned, n elements, pairwise disjoint
- * (ZDO_EALIAS); the current device's LDS size sets the cap. */
+ * of the method). Over n elements (a multiple of 512, >= 0), in tiles of 512
+ * in the step's tile and lane layout, every access non-temporal: each of the
+ * n_reads bf16 buffers reads[j] is read once (n_reads = 8, 16 or 32) and the
+ * three fp32 buffers state0..2 are read. Lane l of a tile holds the 16-byte
+ * chunk [8l, 8l + 8) of each read buffer and the quads [4l, 4l + 4) and
+ * [256 + 4l, 256 + 4l + 4) of each state buffer; x is the XOR of its read
+ * chunks (four 32-bit words). What is then stored, by `stores`:
+ *   ZDO_PROBE_STORE_ALL (2*n_reads + 26 bytes per element, the step's count):
+ *     every state value gains the exponent bits of x[0]^x[1]^x[2]^x[3], and
+ *     quad h of out gets the old master[0] and exp_avg[1] bits of quad h,
+ *     XORed with x[2h] and x[2h+1];
+ *   ZDO_PROBE_STORE_OUT (2*n_reads + 14): the state is not stored; quad h of
+ *     out gets x[2h] ^ S_h and x[2h+1] ^ S_h, S_h the XOR of the 12 state
+ *     words of quad h;
+ *   ZDO_PROBE_STORE_NONE (2*n_reads + 12): nothing but, per tile t, the
+ *     32-bit word at out[2t, 2t+2) = the XOR over the tile's 64 lanes of
+ *     x[0]^x[1]^x[2]^x[3]^S_0^S_1; the rest of out is left as it was.
+ * waves_per_cu caps the workgroups per compute unit (0: no cap). All buffers
+ * device, 16-byte aligned, n elements, pairwise disjoint (ZDO_EALIAS); the
+ * current device's LDS size sets the cap. */
 int zdo_stream_probe(const uint16_t *const *reads, int32_t n_reads, float *state0, float *state1, float *state2,
-                     uint16_t *out, int64_t n, int32_t waves_per_cu, void *stream);
+                     uint16_t *out, int64_t n, int32_t stores, int32_t waves_per_cu, void *stream);
 
 const char *zdo_last_error(void);
 

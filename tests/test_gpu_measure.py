@@ -1,5 +1,6 @@
 """The measurement references on the GPU: zdo_device_copy and
-zdo_stream_probe (the step's stream shape with trivial arithmetic). Not
+zdo_stream_probe (the step's stream shape with trivial arithmetic, in its
+three store modes). Not
 part of the method; checked against the transform include/zdo.h states,
 evaluated with numpy, and for their argument errors."""
 
@@ -35,6 +36,32 @@ def probe_numpy(reads, state, n):
     return new, out
 
 
+def probe_numpy_parts(reads, state, n, stores, out0):
+    """The two store modes without state stores: with PROBE_STORE_OUT quad h
+    of each lane gets x[2h] ^ S_h and x[2h+1] ^ S_h (S_h: XOR of the quad's
+    12 state words); with PROBE_STORE_NONE only word t of out (elements
+    2t, 2t+1) changes, to the XOR over the tile's lanes of
+    x[0]^x[1]^x[2]^x[3]^S_0^S_1."""
+    tiles = n // 512
+    x = np.zeros((tiles, 64, 4), np.uint32)
+    for r in reads:
+        x ^= r[:n].view(np.uint32).reshape(tiles, 64, 4)
+    sx = np.zeros((tiles, 2, 64), np.uint32)
+    for st in state:
+        q = st[:n].view(np.uint32).reshape(tiles, 2, 64, 4)
+        sx ^= q[..., 0] ^ q[..., 1] ^ q[..., 2] ^ q[..., 3]
+    out = out0.copy()
+    if stores == 1:
+        o32 = out.view(np.uint32).reshape(tiles, 2, 64, 2)
+        for h in range(2):
+            o32[:, h, :, 0] = x[..., 2 * h] ^ sx[:, h]
+            o32[:, h, :, 1] = x[..., 2 * h + 1] ^ sx[:, h]
+    else:
+        v = x[..., 0] ^ x[..., 1] ^ x[..., 2] ^ x[..., 3] ^ sx[:, 0] ^ sx[:, 1]
+        out.view(np.uint32)[:tiles] = np.bitwise_xor.reduce(v, axis=1)
+    return out
+
+
 @pytest.mark.parametrize("D", [8, 16, 32])
 def test_stream_probe_transform(gpu, D):
     rng = np.random.default_rng(D)
@@ -52,7 +79,21 @@ def test_stream_probe_transform(gpu, D):
         for x, w in zip(sd, want_s):
             assert np.array_equal(x.cpu().numpy().view(np.uint32), w.view(np.uint32))
         assert np.array_equal(od.view(torch.int16).cpu().numpy().view(np.uint16), want_o)
+    # the store modes that leave the state alone
+    out0 = rng.integers(0, 1 << 16, n, dtype=np.uint32).astype(np.uint16)
+    for stores in (gpu.PROBE_STORE_OUT, gpu.PROBE_STORE_NONE):
+        for x, st in zip(sd, state):
+            x.copy_(torch.from_numpy(st))
+        od.copy_(torch.from_numpy(out0.view(np.int16)))
+        gpu.stream_probe(rd, sd, od, n, 4, stores=stores)
+        for x, st in zip(sd, state):
+            assert np.array_equal(x.cpu().numpy().view(np.uint32), st.view(np.uint32))
+        want_o = probe_numpy_parts(reads, state, n, stores, out0)
+        assert np.array_equal(od.cpu().numpy().view(np.uint16), want_o), f"stores={stores}"
     # errors
+    with pytest.raises(gpu.ZdoError) as e:
+        gpu.stream_probe(rd, sd, od, n, stores=3)
+    assert e.value.code == gpu.EINVAL
     with pytest.raises(gpu.ZdoError) as e:
         gpu.stream_probe(rd[:5], sd, od, n)
     assert e.value.code == gpu.EINVAL

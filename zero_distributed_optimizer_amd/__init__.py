@@ -22,6 +22,8 @@ import numpy as np
 WORLD = 0
 LOCAL = 1
 MAX_REPLICAS = 64
+# zdo_stream_probe's store modes (include/zdo.h)
+PROBE_STORE_ALL, PROBE_STORE_OUT, PROBE_STORE_NONE = 0, 1, 2
 
 OK, EINVAL, EALIGN, EALIAS, EHIP, ENOMEM = 0, -1, -2, -3, -4, -5
 _CODES = {EINVAL: "EINVAL", EALIGN: "EALIGN", EALIAS: "EALIAS", EHIP: "EHIP", ENOMEM: "ENOMEM"}
@@ -126,7 +128,7 @@ def require_library() -> ctypes.CDLL:
                                               vp]
     L.all_gather_params.argtypes = [vp, vp, i32, vp, vp]
     L.zdo_device_copy.argtypes = [vp, vp, i64, vp]
-    L.zdo_stream_probe.argtypes = [vp, i32, vp, vp, vp, vp, i64, i32, vp]
+    L.zdo_stream_probe.argtypes = [vp, i32, vp, vp, vp, vp, i64, i32, i32, vp]
     L.zdo_last_error.argtypes = []
     L.zdo_last_error.restype = ctypes.c_char_p
     for f in ("build_range_map", "zdo_plan_buckets", "zdo_plan_pieces", "plan_buckets", "plan_pieces",
@@ -466,12 +468,14 @@ def device_copy(dst, src, stream=None) -> None:
     _check(require_library().zdo_device_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream(stream, src.device)))
 
 
-def stream_probe(reads, state, out, n: int, waves_per_cu: int = 0, stream=None) -> None:
+def stream_probe(reads, state, out, n: int, waves_per_cu: int = 0, stream=None, stores: int = PROBE_STORE_ALL) -> None:
     """The step's stream shape with trivial arithmetic (zdo_stream_probe): the
-    bf16 tensors `reads` are read, the three float32 tensors `state` read and
-    rewritten, `out` (bf16) written, over n elements (a multiple of 512)."""
+    bf16 tensors `reads` and the three float32 tensors `state` are read over
+    n elements (a multiple of 512); `stores` selects what is then stored:
+    the state rewritten and `out` (bf16) written (PROBE_STORE_ALL), `out`
+    only (PROBE_STORE_OUT), or one word per tile of `out` (PROBE_STORE_NONE)."""
     r = _ptr_list(reads, "reads", n)
     s0, s1, s2 = (_dev_ptr(x, "state", "f32", n) for x in state)
     o = _dev_ptr(out, "out", "bf16", n)
-    _check(require_library().zdo_stream_probe(r, len(reads), s0, s1, s2, o, n, waves_per_cu,
+    _check(require_library().zdo_stream_probe(r, len(reads), s0, s1, s2, o, n, stores, waves_per_cu,
                                               _stream(stream, out.device)))

@@ -736,10 +736,12 @@ int zdo_device_copy(void *dst, const void *src, int64_t bytes, void *stream) {
 }
 
 int zdo_stream_probe(const uint16_t *const *reads, int32_t n_reads, float *state0, float *state1, float *state2,
-                     uint16_t *out, int64_t n, int32_t waves_per_cu, void *stream) {
+                     uint16_t *out, int64_t n, int32_t stores, int32_t waves_per_cu, void *stream) {
     const char *fn = "zdo_stream_probe";
     if (n_reads != 8 && n_reads != 16 && n_reads != 32)
         return fail(ZDO_EINVAL, std::string(fn) + ": n_reads must be 8, 16 or 32");
+    if (stores != ZDO_PROBE_STORE_ALL && stores != ZDO_PROBE_STORE_OUT && stores != ZDO_PROBE_STORE_NONE)
+        return fail(ZDO_EINVAL, std::string(fn) + ": stores must be ZDO_PROBE_STORE_ALL, _OUT or _NONE");
     if (n < 0 || n % kTileElems != 0)
         return fail(ZDO_EINVAL, std::string(fn) + ": n must be a non-negative multiple of 512");
     if (waves_per_cu < 0)
@@ -773,6 +775,7 @@ int zdo_stream_probe(const uint16_t *const *reads, int32_t n_reads, float *state
         hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess)
         return fail(ZDO_EHIP, std::string(fn) + ": no HIP device");
     a.nrep = n_reads;
+    a.stores = stores;
     a.out = out;
     a.ntiles = n / kTileElems;
     return launch_result(launch_probe(a, waves_per_cu, lds, static_cast<hipStream_t>(stream)), fn);

@@ -110,11 +110,13 @@ struct WritebackArgs {
 };
 
 // The step's stream shape with trivial arithmetic (zdo_stream_probe): ntiles
-// tiles of 512 elements of nrep bf16 streams (read), three fp32 streams (read
-// and rewritten) and one bf16 stream (written).
+// tiles of 512 elements of nrep bf16 streams (read), three fp32 streams (read,
+// and rewritten with ZDO_PROBE_STORE_ALL) and one bf16 stream (written with
+// ZDO_PROBE_STORE_ALL or _OUT; one word per tile with _NONE).
 struct ProbeArgs {
     const uint16_t *rep[ZDO_MAX_REPLICAS];
     int32_t nrep;
+    int32_t stores;      // ZDO_PROBE_STORE_*
     float *state[3];
     uint16_t *out;
     int64_t ntiles;

@@ -836,13 +836,15 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a) {
 
 // The step's stream shape with trivial arithmetic (a measurement reference):
 // per 512-element tile, D bf16 streams read by 16-byte chunks, three fp32
-// streams read and rewritten by two quads per lane, one bf16 stream written by
-// quads, every access non-temporal as in the step on a large shard. The bf16
-// words are XORed and the result's exponent bits added to the fp32 values;
-// every loaded byte feeds a stored one, so no load can be dropped. The
-// occupancy bounds are the step's, so that the compiler likewise issues
-// every load of a tile before the first wait.
-template <int D>
+// streams read by two quads per lane, every access non-temporal as in the
+// step on a large shard. kStores selects what is stored (include/zdo.h,
+// ZDO_PROBE_STORE_*): the step's stores (the state rewritten, gaining the
+// exponent bits of the lane's XOR of its chunks, and the bf16 stream
+// written), the bf16 stream only, or one word per tile. Every loaded byte
+// feeds a stored one, so no load can be dropped or narrowed. The occupancy
+// bounds are the step's, so that the compiler likewise issues every load of
+// a tile before the first wait.
+template <int D, int kStores>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(D >= 32 ? 2 : 1, D < 32 ? 4 : 3)))
 void probe_kernel(ProbeArgs a) {
     const int lane = int(threadIdx.x);
@@ -862,14 +864,39 @@ void probe_kernel(ProbeArgs a) {
 #pragma unroll
         for (int j = 1; j < D; ++j)
             x ^= r[j];
-        const float f = __uint_as_float((x[0] ^ x[1] ^ x[2] ^ x[3]) & 0x3f000000u);
+        if constexpr (kStores == ZDO_PROBE_STORE_ALL) {
+            const float f = __uint_as_float((x[0] ^ x[1] ^ x[2] ^ x[3]) & 0x3f000000u);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+            for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int i = 0; i < 3; ++i)
-                st_state<true>(a.state[i] + kb + h * (kTileElems / 2) + 4 * lane, s[h][i] + f);
-            st8_out(a.out + kb + h * (kTileElems / 2) + 4 * lane,
-                    u32x2{__float_as_uint(s[h][0][0]) ^ x[2 * h], __float_as_uint(s[h][1][1]) ^ x[2 * h + 1]});
+                for (int i = 0; i < 3; ++i)
+                    st_state<true>(a.state[i] + kb + h * (kTileElems / 2) + 4 * lane, s[h][i] + f);
+                st8_out(a.out + kb + h * (kTileElems / 2) + 4 * lane,
+                        u32x2{__float_as_uint(s[h][0][0]) ^ x[2 * h], __float_as_uint(s[h][1][1]) ^ x[2 * h + 1]});
+            }
+        } else {
+            uint32_t sx[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                sx[h] = 0;
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        sx[h] ^= __float_as_uint(s[h][i][c]);
+            }
+            if constexpr (kStores == ZDO_PROBE_STORE_OUT) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    st8_out(a.out + kb + h * (kTileElems / 2) + 4 * lane, u32x2{x[2 * h] ^ sx[h], x[2 * h + 1] ^ sx[h]});
+            } else {
+                uint32_t v = x[0] ^ x[1] ^ x[2] ^ x[3] ^ sx[0] ^ sx[1];
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1)
+                    v ^= uint32_t(__shfl_xor(int(v), off, 64));
+                if (lane == 0)
+                    *reinterpret_cast<uint32_t *>(a.out + 2 * tile) = v;
+            }
         }
     }
 }
@@ -1111,10 +1138,16 @@ hipError_t launch_probe(const ProbeArgs &a, int waves_per_cu, int lds_per_cu, hi
         return hipSuccess;
     const dim3 grid(grid_for(a.ntiles)), block(kBlock);
     const unsigned lds = lds_for_waves(lds_per_cu, waves_per_cu);
-    switch (a.nrep) {
-    case 8: hipLaunchKernelGGL(probe_kernel<8>, grid, block, lds, stream, a); break;
-    case 16: hipLaunchKernelGGL(probe_kernel<16>, grid, block, lds, stream, a); break;
-    case 32: hipLaunchKernelGGL(probe_kernel<32>, grid, block, lds, stream, a); break;
+    switch (a.nrep * 4 + a.stores) {
+    case 8 * 4 + ZDO_PROBE_STORE_ALL: hipLaunchKernelGGL((probe_kernel<8, ZDO_PROBE_STORE_ALL>), grid, block, lds, stream, a); break;
+    case 8 * 4 + ZDO_PROBE_STORE_OUT: hipLaunchKernelGGL((probe_kernel<8, ZDO_PROBE_STORE_OUT>), grid, block, lds, stream, a); break;
+    case 8 * 4 + ZDO_PROBE_STORE_NONE: hipLaunchKernelGGL((probe_kernel<8, ZDO_PROBE_STORE_NONE>), grid, block, lds, stream, a); break;
+    case 16 * 4 + ZDO_PROBE_STORE_ALL: hipLaunchKernelGGL((probe_kernel<16, ZDO_PROBE_STORE_ALL>), grid, block, lds, stream, a); break;
+    case 16 * 4 + ZDO_PROBE_STORE_OUT: hipLaunchKernelGGL((probe_kernel<16, ZDO_PROBE_STORE_OUT>), grid, block, lds, stream, a); break;
+    case 16 * 4 + ZDO_PROBE_STORE_NONE: hipLaunchKernelGGL((probe_kernel<16, ZDO_PROBE_STORE_NONE>), grid, block, lds, stream, a); break;
+    case 32 * 4 + ZDO_PROBE_STORE_ALL: hipLaunchKernelGGL((probe_kernel<32, ZDO_PROBE_STORE_ALL>), grid, block, lds, stream, a); break;
+    case 32 * 4 + ZDO_PROBE_STORE_OUT: hipLaunchKernelGGL((probe_kernel<32, ZDO_PROBE_STORE_OUT>), grid, block, lds, stream, a); break;
+    case 32 * 4 + ZDO_PROBE_STORE_NONE: hipLaunchKernelGGL((probe_kernel<32, ZDO_PROBE_STORE_NONE>), grid, block, lds, stream, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

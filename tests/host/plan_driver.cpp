@@ -74,6 +74,13 @@ int main() {
     if (build_range_map(nullptr, 0, 10, 2, 0, &p) == ZDO_OK) return 10;
     if (build_range_map(s, 1, 10, 65, 0, &p) == ZDO_OK) return 11;
     if (zdo_device_copy(nullptr, nullptr, 15, nullptr) == ZDO_OK) return 12;
+    // the stream probe's argument checks come before any device call
+    const uint16_t *rr[8] = {};
+    if (zdo_stream_probe(rr, 8, nullptr, nullptr, nullptr, nullptr, 512, 3, 0, nullptr) == ZDO_OK) return 16;
+    if (zdo_stream_probe(rr, 7, nullptr, nullptr, nullptr, nullptr, 512, ZDO_PROBE_STORE_ALL, 0, nullptr) == ZDO_OK)
+        return 17;
+    if (zdo_stream_probe(rr, 8, nullptr, nullptr, nullptr, nullptr, 500, ZDO_PROBE_STORE_NONE, 0, nullptr) == ZDO_OK)
+        return 18;
     std::printf("ok: 3000 plans, %ld pieces checked\n", checked);
     return 0;
 }

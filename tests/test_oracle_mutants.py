@@ -68,6 +68,8 @@ def _layout_pins():
         lambda: TS.test_all_gather_closes_the_zero1_loop(1),
         lambda: TS.test_rank_norm_sq_exact_and_summing_to_the_global_norm(0),
         lambda: TS.test_rank_norm_sq_exact_and_summing_to_the_global_norm(1),
+        lambda: TS.test_rank_state_is_the_zero1_share("frag"),
+        lambda: TS.test_rank_state_is_the_zero1_share("gpt2_small"),
     ]
 
 
@@ -208,6 +210,11 @@ PY_MUTANTS = {
          "        total",
          "    for world, base in L.rank_ranges(layout, rank):\n        g0, g1 = _span(grad_coords, world, base)\n"
          "        total")]),
+    "shard views a whole line further apart than the phase needs": ("layout", [
+        ("base = end + (start - end) % SHARD_PHASE", "base = end + (start - end) % SHARD_PHASE + SHARD_PHASE")]),
+    "owned elements counted over the whole ranges, padding included": ("layout", [
+        ("    return sum(p.gbuf_world.size for p in rank_pieces(layout, rank))",
+         "    return sum(r.size for r, _ in rank_ranges(layout, rank))")]),
     "reduce-scatter over the parameter pieces only": ("step", [
         ("    for b, (world, base) in enumerate(L.rank_ranges(layout, rank)):",
          "    for b, (world, base) in enumerate([(pc.gbuf_world, pc.shard_offset)\n"
